@@ -1,0 +1,32 @@
+"""CPU oracle for the Mixtral sparse MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, links or runs
+anything under this directory: only the tests, the smoke check and the
+benchmark's CPU-baseline leg do.  It shares no code with the HIP library; the
+one module both sides use is the seeded input generator in ``synth``.
+
+Every function restates, in plain numpy, a passage of the pages it cites
+(page title + section / equation).  Results the pages fix (parameter counts,
+closed forms, invariants) pin it in ``tests/test_oracle_pins.py``.
+
+Parity unpinned: the bf16 output values of the full layer have no external
+vector; they are checked only through the invariants and special cases
+listed in the pin tests (identity case, 28-pair brute force, fp64 shadow).
+"""
+from .moe_ref import (  # noqa: F401
+    aux_loss_ref,
+    block_forward_ref,
+    dispatch_ref,
+    expert_swiglu,
+    moe_forward_expert_loop,
+    moe_forward_token_loop,
+    moe_forward_tokens,
+    rmsnorm_ref,
+    route_ref,
+    router_logits,
+    silu,
+    top2,
+    topk_softmax,
+    widen,
+)
+from .params import mistral_param_count, moe_model_param_counts  # noqa: F401

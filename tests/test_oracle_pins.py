@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: numbers the
+pages print, closed forms, invariants, brute force on tiny inputs, or an
+independent library formulation (torch / scipy / math.fsum).  The last block
+plants mistakes into copies of oracle functions (on the CPU) and checks that
+the pins catch them.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import moe_ref
+from oracle.params import mistral_param_count, moe_model_param_counts
+from synth import CONFIGS, generate
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "param_counts.txt")
+
+
+# ---------------------------------------------------------------------------
+# parameter counts (the pages' exact integers)
+# ---------------------------------------------------------------------------
+def _golden():
+    out = {}
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            model, part, value = line.split()
+            out[(model, part)] = int(value)
+    return out
+
+
+def test_param_counts_match_pages():
+    g = _golden()
+    mix = moe_model_param_counts(4096, 32, 32, 8, 128, 14336, 8, 2, 32000)
+    teach = moe_model_param_counts(256, 4, 4, 2, 64, 1024, 8, 2, 1000, bias=True)
+    e16 = moe_model_param_counts(4096, 32, 32, 8, 128, 14336, 16, 2, 32000)
+    got = {("mixtral", p): v for p, v in mix.items()}
+    got.update({("teach", p): v for p, v in teach.items()})
+    got.update({("e16", p): v for p, v in e16.items()})
+    got[("mistral", "total")] = mistral_param_count(4096, 32, 32, 8, 128, 14336, 32000)
+    got[("mistral_mha", "total")] = mistral_param_count(4096, 32, 32, 32, 128, 14336, 32000)
+    got[("mistral_teach", "total")] = mistral_param_count(256, 4, 4, 2, 64, 1024, 1000, bias=True)
+    assert len(g) >= 20
+    for key, value in g.items():
+        assert got[key] == value, key
+
+
+def test_ffn_share_of_layer_flops():
+    # "Mixtral" page, exercise 3: FFN share ~ 0.894 of a layer's non-quadratic FLOPs.
+    c = moe_model_param_counts(4096, 32, 32, 8, 128, 14336, 8, 2, 32000)
+    share = 2 * c["expert"] / (c["attention_layer"] + c["router_layer"] + 2 * c["expert"])
+    assert abs(share - 0.894) < 5e-4
+
+
+def test_expert_work_is_k_over_E():
+    # "Алгоритм": experts process kN rows, k/E = 1/4 of all-experts-on-all-tokens.
+    rng = np.random.default_rng(3)
+    g = rng.standard_normal((500, 8)).astype(np.float32)
+    idx = oracle.top2(g)
+    off, _, _ = oracle.dispatch_ref(idx, 8)
+    assert off[-1] == 2 * 500
+    assert off[-1] / (8 * 500) == 0.25
+
+
+# ---------------------------------------------------------------------------
+# router logits: fp32 within the dot-product error bound of the exact value
+# ---------------------------------------------------------------------------
+def test_router_logits_within_dot_product_bound():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = generate(cfg)
+    x, wg = inp["x"], inp["w_gate"]
+    g = oracle.router_logits(x, wg)
+    d = x.shape[1]
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    for t in range(0, x.shape[0], 7):
+        for e in range(wg.shape[0]):
+            prods = [float(a) * float(b) for a, b in zip(x[t], wg[e])]  # exact in fp64
+            exact = math.fsum(prods)
+            bound = gamma * math.fsum(abs(p) for p in prods)
+            assert abs(float(g[t, e]) - exact) <= bound + 1e-30
+
+
+def test_router_bias_is_added_per_expert():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 16)).astype(np.float32)
+    wg = rng.standard_normal((4, 16)).astype(np.float32)
+    b = np.array([1.0, -2.0, 0.5, 3.0], np.float32)
+    diff = oracle.router_logits(x, wg, b) - oracle.router_logits(x, wg)
+    np.testing.assert_allclose(diff, np.broadcast_to(b, diff.shape), atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# top-2: brute force over the 28 expert pairs, ties, distinctness
+# ---------------------------------------------------------------------------
+def _pair_argmax(gt):
+    E = len(gt)
+    return max(itertools.combinations(range(E), 2), key=lambda p: (gt[p[0]] + gt[p[1]]))
+
+
+def test_28_pairs():
+    assert len(list(itertools.combinations(range(8), 2))) == 28 == math.comb(8, 2)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_top2_set_equals_best_pair(seed):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((400, 8)).astype(np.float32)
+    idx = oracle.top2(g)
+    for t in range(g.shape[0]):
+        srt = np.sort(g[t])[::-1]
+        if srt[1] == srt[2]:
+            continue
+        assert set(idx[t].tolist()) == set(_pair_argmax(g[t].astype(np.float64)))
+        assert idx[t, 0] != idx[t, 1]
+        assert g[t, idx[t, 0]] >= g[t, idx[t, 1]]
+
+
+def test_top2_tie_rule():
+    g = np.array([[1, 3, 3, 0, 0, 0, 0, 0],
+                  [5, 5, 5, 5, 5, 5, 5, 5],
+                  [0, 0, 0, 0, 0, 0, 2, 2],
+                  [0, 9, 0, 0, 0, 0, 0, 1]], np.float32)
+    idx = oracle.top2(g)
+    assert idx.tolist() == [[1, 2], [0, 1], [6, 7], [1, 7]]
+
+
+# ---------------------------------------------------------------------------
+# combine weights: sum to one, closed form, the HF softmax-then-renormalise form
+# ---------------------------------------------------------------------------
+def test_weights_sum_to_one_and_match_sigmoid_and_hf_form():
+    rng = np.random.default_rng(5)
+    g = (rng.standard_normal((1000, 8)) * 3).astype(np.float32)
+    idx = oracle.top2(g)
+    w = oracle.topk_softmax(g, idx)
+    assert w.dtype == np.float32
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=2 ** -23 * 2)
+    sel = np.take_along_axis(g.astype(np.float64), idx, axis=1)
+    # closed form: w0 = sigmoid(g_s0 - g_s1)
+    np.testing.assert_allclose(w[:, 0], scipy.special.expit(sel[:, 0] - sel[:, 1]), atol=1e-6)
+    # HF form: softmax over all E, keep top-2, renormalise (the pages state equality)
+    full = scipy.special.softmax(g.astype(np.float64), axis=1)
+    keep = np.take_along_axis(full, idx, axis=1)
+    np.testing.assert_allclose(w, keep / keep.sum(axis=1, keepdims=True), atol=1e-6)
+
+
+def test_weights_are_zero_outside_selected_pair_via_minus_inf():
+    # Top2 sets non-selected logits to -inf; a softmax over the full vector
+    # then gives the same two weights and exact zeros elsewhere.
+    rng = np.random.default_rng(6)
+    g = rng.standard_normal((50, 8)).astype(np.float64)
+    idx = oracle.top2(g)
+    w = oracle.topk_softmax(g, idx, dtype=np.float64)
+    masked = np.full_like(g, -np.inf)
+    np.put_along_axis(masked, idx, np.take_along_axis(g, idx, axis=1), axis=1)
+    sm = scipy.special.softmax(masked, axis=1)
+    for t in range(g.shape[0]):
+        assert np.count_nonzero(sm[t]) == 2
+        np.testing.assert_allclose(sm[t, idx[t]], w[t], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# dispatch: invariants and a nested-loop brute force
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E", [(1, 8), (37, 8), (256, 8), (100, 4)])
+def test_dispatch_invariants_and_bruteforce(T, E):
+    rng = np.random.default_rng(T)
+    g = rng.standard_normal((T, E)).astype(np.float32)
+    g[:, 2 % E] -= 50.0  # one expert never selected
+    idx = oracle.top2(g)
+    off, st, inv = oracle.dispatch_ref(idx, E)
+    assert off[0] == 0 and off[-1] == 2 * T
+    assert np.all(np.diff(off) >= 0)
+    assert off[(2 % E) + 1] - off[2 % E] == 0
+    counts = np.bincount(st, minlength=T)
+    assert np.all(counts == 2)
+    for e in range(E):
+        rows = st[off[e]:off[e + 1]]
+        assert np.all(np.diff(rows) > 0)
+    # brute force: walk experts, then tokens, then slots
+    expect = []
+    for e in range(E):
+        for t in range(T):
+            for s in range(2):
+                if idx[t, s] == e:
+                    expect.append((t, s))
+    assert st.tolist() == [t for t, _ in expect]
+    for r, (t, s) in enumerate(expect):
+        assert inv[t, s] == r
+
+
+# ---------------------------------------------------------------------------
+# layer output: identity case, 28-pair brute force, O1 vs O2, fp64 shadow
+# ---------------------------------------------------------------------------
+def _torch_swiglu(u, w1, w3, w2):
+    return (torch.nn.functional.silu(u @ w1.T) * (u @ w3.T)) @ w2.T
+
+
+def _tiny(seed, T=12, d=16, d_ff=24, E=8):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, d)).astype(np.float32)
+    wg = rng.standard_normal((E, d)).astype(np.float32)
+    w1 = (rng.standard_normal((E, d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    w3 = (rng.standard_normal((E, d_ff, d)) / math.sqrt(d)).astype(np.float32)
+    w2 = (rng.standard_normal((E, d, d_ff)) / math.sqrt(d_ff)).astype(np.float32)
+    return x, wg, w1, w3, w2
+
+
+def test_identity_when_all_experts_equal():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = generate(cfg)
+    w1 = np.broadcast_to(inp["w1"][3], inp["w1"].shape).copy()
+    w3 = np.broadcast_to(inp["w3"][3], inp["w3"].shape).copy()
+    w2 = np.broadcast_to(inp["w2"][3], inp["w2"].shape).copy()
+    y, _ = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], None, w1, w3, w2)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    dense = _torch_swiglu(t(inp["x"]), t(w1[0]), t(w3[0]), t(w2[0])).numpy()
+    assert np.max(np.abs(y - dense)) <= 1e-5 * np.max(np.abs(dense))
+
+
+def _pair_bruteforce_torch(x, wg, b, w1, w3, w2):
+    """y_t from the best of the 28 pairs, computed with torch in float64."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    X, WG = t(x), t(wg)
+    G = X @ WG.T + (t(b) if b is not None else 0)
+    T, E = G.shape
+    y = torch.zeros_like(X)
+    ok = np.ones(T, bool)
+    for tt in range(T):
+        gt = G[tt]
+        srt = torch.sort(gt, descending=True).values
+        ok[tt] = bool(srt[1] - srt[2] > 1e-3)
+        i, j = _pair_argmax(gt.tolist())
+        wts = torch.softmax(torch.stack([gt[i], gt[j]]), dim=0)
+        for wgt, e in zip(wts, (i, j)):
+            y[tt] += wgt * _torch_swiglu(X[tt:tt + 1], t(w1[e]), t(w3[e]), t(w2[e]))[0]
+    return y.numpy(), ok
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_output_equals_28_pair_bruteforce(seed):
+    x, wg, w1, w3, w2 = _tiny(seed)
+    b = np.linspace(-0.5, 0.5, 8).astype(np.float32)
+    y, _ = oracle.moe_forward_token_loop(x, wg, b, w1, w3, w2)
+    ref, ok = _pair_bruteforce_torch(x, wg, b, w1, w3, w2)
+    assert ok.sum() >= len(ok) // 2
+    err = np.max(np.abs(y[ok] - ref[ok]))
+    assert err <= 1e-5 * np.max(np.abs(ref[ok]))
+
+
+def test_token_loop_equals_expert_loop_tiny_config():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = generate(cfg)
+    args = (inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    y1, (g1, i1, w1) = oracle.moe_forward_token_loop(*args)
+    y2, (g2, i2, w2) = oracle.moe_forward_expert_loop(*args)
+    assert np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    assert np.max(np.abs(y1 - y2)) <= 1e-6 * np.max(np.abs(y2))
+
+
+def test_fp32_oracle_within_fp64_shadow():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = generate(cfg)
+    args = (inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    y32, (g32, i32, _) = oracle.moe_forward_token_loop(*args)
+    y64, (g64, i64, _) = oracle.moe_forward_token_loop(*args, dtype=np.float64)
+    srt = np.sort(g64, axis=1)[:, ::-1]
+    clear = (srt[:, 1] - srt[:, 2]) > 1e-4
+    assert clear.mean() > 0.9
+    for t in np.nonzero(clear)[0]:
+        assert set(i32[t]) == set(i64[t])
+    assert np.max(np.abs(y32[clear] - y64[clear])) <= 1e-5 * np.max(np.abs(y64))
+
+
+def test_k_equals_E_is_full_softmax_mixture():
+    # With E = k = 2 the layer is the softmax-weighted sum of both experts.
+    x, wg, w1, w3, w2 = _tiny(9, E=2)
+    y, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, w2, k=2)
+    g = x.astype(np.float64) @ wg.T.astype(np.float64)
+    p = scipy.special.softmax(g, axis=1)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    ref = sum(p[:, e:e + 1] * _torch_swiglu(t(x), t(w1[e]), t(w3[e]), t(w2[e])).numpy() for e in range(2))
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_silu_matches_torch():
+    z = np.linspace(-30, 30, 2001)
+    np.testing.assert_allclose(oracle.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-12, atol=1e-300)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and the residual sublayer
+# ---------------------------------------------------------------------------
+def test_rmsnorm_matches_torch_and_closed_form():
+    rng = np.random.default_rng(2)
+    z = rng.standard_normal((9, 64)) * 3
+    gamma = rng.standard_normal(64)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(z), (64,), torch.from_numpy(gamma), eps=1e-5)
+    np.testing.assert_allclose(oracle.rmsnorm_ref(z, gamma, 1e-5, np.float64), ref.numpy(), rtol=1e-12)
+    c = 0.01
+    row = np.full((1, 32), c)
+    out = oracle.rmsnorm_ref(row, None, 1e-5, np.float64)
+    np.testing.assert_allclose(out, c / math.sqrt(c * c + 1e-5), rtol=1e-14)
+
+
+def test_block_is_residual_plus_moe():
+    x, wg, w1, w3, w2 = _tiny(4)
+    gamma = np.ones(x.shape[1], np.float32)
+    out, u, _ = oracle.block_forward_ref(x, gamma, 1e-5, wg, None, w1, w3, np.zeros_like(w2))
+    assert np.array_equal(out, x)  # zero down-projection: the sublayer adds exactly 0
+    w1e = np.broadcast_to(w1[0], w1.shape).copy()
+    w3e = np.broadcast_to(w3[0], w3.shape).copy()
+    w2e = np.broadcast_to(w2[0], w2.shape).copy()
+    out, _, _ = oracle.block_forward_ref(x, gamma, 1e-5, wg, None, w1e, w3e, w2e)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    un = torch.nn.functional.rms_norm(t(x), (x.shape[1],), eps=1e-5)
+    ref = t(x) + _torch_swiglu(un, t(w1[0]), t(w3[0]), t(w2[0]))
+    assert np.max(np.abs(out - ref.numpy())) <= 1e-5 * np.max(np.abs(ref.numpy()))
+
+
+# ---------------------------------------------------------------------------
+# load-balancing loss closed forms
+# ---------------------------------------------------------------------------
+def test_aux_loss_uniform_load_equals_alpha_k():
+    E, k, alpha = 8, 2, 0.01
+    v = np.array([3.0, 2.0, 0.5, 0.1, -0.2, -1.0, -1.5, -2.0])
+    g = np.stack([np.roll(v, s) for s in range(E)])  # each expert at each rank once
+    assert abs(oracle.aux_loss_ref([g, g[::-1]], E, k, alpha) - alpha * k) < 1e-12
+
+
+def test_aux_loss_collapsed_router_equals_alpha_E():
+    E, k, alpha = 8, 2, 0.5
+    g = np.full((10, E), -1e9)
+    g[:, 0] = 4.0
+    g[:, 1] = 4.0
+    # f_{1,0} = f_{2,1} = 1 and P_0 = P_1 = 1/2  ->  alpha * E * (1/2 + 1/2)
+    assert abs(oracle.aux_loss_ref([g], E, k, alpha) - alpha * E) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: a mutated copy of the oracle must fail a pin
+# ---------------------------------------------------------------------------
+def _mut_silu_sign(z):
+    return z / (1 + np.exp(z))
+
+
+def _mut_swap_gate_up(u, w1_e, w3_e, w2_e, dtype=np.float32):
+    return _orig_expert(u, w3_e, w1_e, w2_e, dtype)
+
+
+def _mut_transpose_down(u, w1_e, w3_e, w2_e, dtype=np.float32):
+    u = moe_ref.widen(u, dtype)
+    h = moe_ref.silu(u @ moe_ref.widen(w1_e, dtype).T) * (u @ moe_ref.widen(w3_e, dtype).T)
+    w2 = moe_ref.widen(w2_e, dtype)
+    return (h @ w2.reshape(w2.shape[1], w2.shape[0])).astype(dtype)
+
+
+def _mut_smallest(g, k=2):
+    return np.argsort(g, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def _mut_swap_slots(g, idx, dtype=np.float32):
+    return _orig_softmax(g, idx, dtype)[:, ::-1].copy()
+
+
+def _mut_no_renorm(g, idx, dtype=np.float32):
+    sel = np.take_along_axis(g.astype(dtype), idx.astype(np.int64), axis=1)
+    return np.exp(sel).astype(dtype)
+
+
+_orig_expert = moe_ref.expert_swiglu
+_orig_softmax = moe_ref.topk_softmax
+
+
+@pytest.mark.parametrize("name,target,mutant", [
+    ("silu sign", "silu", _mut_silu_sign),
+    ("gate/up swapped", "expert_swiglu", _mut_swap_gate_up),
+    ("down projection mis-laid", "expert_swiglu", _mut_transpose_down),
+    ("bottom-2 instead of top-2", "top2", _mut_smallest),
+    ("weights on the wrong slots", "topk_softmax", _mut_swap_slots),
+    ("softmax not normalised", "topk_softmax", _mut_no_renorm),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, target, mutant):
+    monkeypatch.setattr(moe_ref, target, mutant)
+    x, wg, w1, w3, w2 = _tiny(0, d=16, d_ff=16)
+    y, _ = moe_ref.moe_forward_token_loop(x, wg, None, w1, w3, w2)
+    monkeypatch.undo()
+    ref, ok = _pair_bruteforce_torch(x, wg, None, w1, w3, w2)
+    err = np.max(np.abs(y[ok] - ref[ok]))
+    assert err > 1e-3 * np.max(np.abs(ref[ok])), name
