@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mixtral sparse MoE feed-forward layer on one MI355X.
+
+One step = one full layer forward (router + top-2 softmax, dispatch, expert
+SwiGLU up/down, weighted combine) through the C ABI's moe_forward on inputs
+already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--secondary NAME|none]
+                    [--no-cpu-baseline]
+
+The default workload is the Mixtral 8x7B layer in the decode regime (T = 16,
+HBM-bound); the prefill layer (T = 4096, MFMA-bound) is measured too and
+reported under "secondary".  Per-kernel durations come from HIP events that
+moe_forward records on its own stream between its kernels (timing points of
+the C ABI); the roofline fraction is that of the dominant kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-FFN layer tokens/s + % of MFMA/HBM roofline, Mixtral shapes, T=16/4096"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
+KERNELS = ["router", "dispatch", "expert_up", "expert_down", "combine"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "router": "router.hip", "dispatch": "dispatch.hip", "expert_up": "expert_ffn.hip",
+    "expert_down": "expert_ffn.hip", "combine": "combine.hip",
+}
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _event(hip):
+    ev = ctypes.c_void_p()
+    assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+    return ev
+
+
+def _elapsed_ms(hip, a, b) -> float:
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return float(ms.value)
+
+
+def _src_sha(name: str) -> str:
+    path = os.path.join(ROOT, "sparse_mixture_experts_wave_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    absent or taken on a different version of the kernel's source."""
+    try:
+        entry = json.load(open(TRAFFIC_FILE))[workload][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if entry.get("src_sha") != _src_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def work_model(cfg, counts):
+    """Algorithmic bytes and FLOPs per kernel launch (no padding, no re-reads)."""
+    T, d, d_ff, E, k = cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k
+    es = 2 if cfg.dtype == "bf16" else 4
+    rows = T * k
+    touched = int(sum(1 for c in counts if c > 0))
+    up_bytes = touched * 2 * d_ff * d * es + T * d * es + rows * d_ff * es
+    down_bytes = touched * d * d_ff * es + rows * d_ff * es + rows * d * 4
+    return {
+        "touched_experts": touched,
+        "router": {"flops": 2 * T * d * E, "bytes": T * d * es + E * d * 4 + T * k * 8},
+        "dispatch": {"flops": 0, "bytes": T * k * 4 * 3 + (E + 1) * 4},
+        "expert_up": {"flops": 4 * rows * d * d_ff, "bytes": up_bytes},
+        "expert_down": {"flops": 2 * rows * d * d_ff, "bytes": down_bytes},
+        "combine": {"flops": 3 * rows * d, "bytes": rows * d * 4 + T * d * es + T * k * 8},
+        "layer": {"flops": 6 * rows * d * d_ff + 2 * T * d * E,
+                  "bytes": touched * 3 * d * d_ff * es + E * d * 4 + 2 * T * d * es},
+    }
+
+
+def measure(cfg, steps: int, warmup: int):
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_wave_amd as moe
+    from sparse_mixture_experts_wave_amd import _lib
+    from synth import generate_torch
+
+    lib = moe.load()
+    hip = _hip()
+    dev = torch.device("cuda:0")
+    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    dv = generate_torch(cfg, dev)
+    shape = moe.make_shape(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, dv["x"].dtype)
+    ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(dv["x"])
+    args = (dv["x"], dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
+
+    def step():
+        moe.moe_forward(*args, out=y, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Plain timed region (no per-kernel events).
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    plain_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # Timed region with the C ABI timing points on the launch stream.
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    evs = [[_event(hip) for _ in range(_lib.MOE_TIMING_POINTS)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        arr = (ctypes.c_void_p * _lib.MOE_TIMING_POINTS)(*[e.value for e in evs[i]])
+        _lib.check(lib.moe_set_timing_events(arr, _lib.MOE_TIMING_POINTS))
+        step()
+    _lib.check(lib.moe_set_timing_events(None, 0))
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = [_elapsed_ms(hip, e[0], e[-1]) for e in evs]
+    per_kernel = {name: statistics.fmean(_elapsed_ms(hip, e[j], e[j + 1]) for e in evs)
+                  for j, name in enumerate(KERNELS)}
+    for e in evs:
+        for ev in e:
+            hip.hipEventDestroy(ev)
+
+    # Expert loads (outside the timed region).
+    idx, _, _ = moe.moe_route(dv["x"], dv["w_gate"], dv["bias"])
+    off, _, _ = moe.moe_dispatch(idx, cfg.E)
+    counts = np.diff(off.cpu().numpy()).tolist()
+    work = work_model(cfg, counts)
+    return {
+        "cfg": cfg, "inputs": dv, "y": y, "ms_per_step": wall_ms, "ms_per_step_events": statistics.fmean(step_ms),
+        "ms_per_step_plain": plain_ms, "per_kernel_ms": per_kernel, "counts": counts, "work": work,
+    }
+
+
+def roofline(res):
+    cfg, work, pk = res["cfg"], res["work"], res["per_kernel_ms"]
+    dom = max(("expert_up", "expert_down"), key=lambda n: pk[n])
+    t = pk[dom] * 1e-3
+    if cfg.T <= 64:  # decode regime: weight reads dominate
+        achieved = work[dom]["bytes"] / t / 1e9
+        peak, unit, bound = PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved = work[dom]["flops"] / t / 1e12
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+        unit, bound = "TFLOP/s", "mfma"
+    return {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom),
+            "kernel_ms": round(pk[dom], 4)}
+
+
+def cpu_baseline(res, max_tokens: int):
+    """The CPU oracle (expert-loop form, numpy fp32) on a bounded sample of the
+    same workload, on this host's cores: tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    def host(t):
+        if t is None:
+            return None
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    cfg, dv = res["cfg"], res["inputs"]
+    n = min(cfg.T, max_tokens)
+    x = host(dv["x"][:n])
+    args = (x, host(dv["w_gate"]), host(dv["bias"]), host(dv["w1"]), host(dv["w3"]), host(dv["w2"]))
+    try:
+        import threadpoolctl
+        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    print(f"[bench] cpu oracle on {n} tokens of {cfg.name}", file=sys.stderr, flush=True)
+    oracle.moe_forward_expert_loop(*args)  # warm-up
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.moe_forward_expert_loop(*args)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": round(n / med, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} tokens of {cfg.name} (numpy fp32 expert-loop oracle, weights widened from bf16 "
+                      f"inside), 1 warm-up + 3 timed, median {med:.2f} s"}
+
+
+def summarize(res):
+    cfg, work = res["cfg"], res["work"]
+    ms = res["ms_per_step"]
+    return {
+        "workload": cfg.name, "T": cfg.T, "tokens_per_s": round(cfg.T / (ms * 1e-3), 2), "ms_per_step": round(ms, 4),
+        "layer_tflops": round(work["layer"]["flops"] / (ms * 1e-3) / 1e12, 2),
+        "layer_gbs": round(work["layer"]["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "roofline": roofline(res),
+        "per_kernel_ms": {k: round(v, 4) for k, v in res["per_kernel_ms"].items()},
+        "rows_per_expert": res["counts"], "touched_experts": work["touched_experts"],
+        "ms_per_step_without_timing_events": round(res["ms_per_step_plain"], 4),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="mixtral_decode_t16")
+    ap.add_argument("--secondary", default="mixtral_prefill_t4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (the layer is built and "
+              "measured on a single MI355X; multi-GPU sharding is a design note, not a run)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth import CONFIGS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[a.config]
+    res = measure(cfg, a.steps, a.warmup)
+    prim = summarize(res)
+    cpu = None if a.no_cpu_baseline else cpu_baseline(res, a.cpu_tokens)
+    del res["inputs"]
+    sec = None
+    if a.secondary and a.secondary != "none" and a.secondary != a.config:
+        torch.cuda.empty_cache()
+        r2 = measure(CONFIGS[a.secondary], max(5, a.steps // 2), a.warmup)
+        sec = summarize(r2)
+        del r2
+    out = {
+        "metric": METRIC, "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded, Mixtral-shaped, random weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "k": cfg.k,
+                   "parallelism": "single GPU"},
+        "roofline": prim["roofline"], "cpu_baseline": cpu, "detail": prim, "secondary": sec,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) Mixtral sparse MoE feed-forward layer.
+ *
+ * The layer (the "Mixtral" textbook page, section "Научный вклад", layer
+ * formula, and section "Прямой проход в формулах", MoE equation):
+ *
+ *     g   = x W_g                   router logits, one per expert
+ *     S   = the k largest logits    (k = 2; the others count as -inf)
+ *     w_i = e^{g_i} / sum_{j in S} e^{g_j}          (float32)
+ *     y   = sum_{i in S} w_i (SiLU(x W1_i) * (x W3_i)) W2_i
+ *
+ * with W1 = gate, W3 = up, W2 = down (same page, section "Загрузка весов
+ * HuggingFace").  The steps map onto the entry points as the page's
+ * expert-major algorithm (section "Алгоритм") splits them: route, dispatch the
+ * tokens of each expert, run each expert on its rows, combine the weighted
+ * outputs back in token order.  Dropless: every token gets exactly k rows.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer is a device pointer, allocated and owned by the
+ *   caller; the library allocates nothing and keeps no state between calls
+ *   apart from cached device properties.  Inputs are read only; outputs are
+ *   fully overwritten, never accumulated into.  Every non-NULL pointer must be
+ *   16-byte aligned.
+ * Layout.  Row-major, reduction dimension contiguous (nn.Linear):
+ *   x [T][d], w_gate [E][d] fp32, w1 and w3 [E][d_ff][d], w2 [E][d][d_ff].
+ *   bf16 values are raw 16-bit patterns (uint16).
+ * Streams.  Every call is asynchronous on `stream` (a hipStream_t passed as
+ *   void*; NULL is the default stream).  No call synchronises with the host
+ *   or copies device data to the host, so sequences can be graph-captured.
+ * Errors.  Arguments are validated on the host before anything is launched;
+ *   a failed call launches nothing and sets a thread-local message readable
+ *   with moe_last_error().  T == 0 returns MOE_OK without launching.
+ *   MOE_ERR_INVALID_ARG: NULL/misaligned pointer, T < 0, d or d_ff not a
+ *     positive multiple of 64 (d <= 32768, d_ff <= 65536), E outside 2..64,
+ *     k outside 1..E (the pages' constructor raises ValueError for this),
+ *     workspace too small.
+ *   MOE_ERR_UNSUPPORTED: k != 2, E not a power of two, or an (act, wt)
+ *     dtype pair other than (F32, F32) and (BF16, BF16).
+ *   MOE_ERR_HIP: a HIP launch failed.
+ * Precision.  Router logits, the top-k softmax and the combine weights are
+ *   fp32 (the pages compute the router softmax in float32).  Expert GEMMs
+ *   accumulate in fp32; with bf16 weights the SwiGLU intermediate h is
+ *   rounded to bf16 and y_sorted is fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_HIP = 3
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer shape.  The pages' constructor arguments: T = batch * seq tokens,
+ * d = emb_size, d_ff = hidden_dim, E = num_experts, k = top_k_experts.
+ * act is the dtype of x / y (and of the residual stream), wt of w1/w3/w2. */
+typedef struct {
+  int64_t T;
+  int32_t d;
+  int32_t d_ff;
+  int32_t E;
+  int32_t k;
+  int32_t act; /* moe_dtype */
+  int32_t wt;  /* moe_dtype */
+} moe_shape;
+
+/* Bytes of workspace moe_forward and moe_block_forward need (256-byte
+ * aligned sub-buffers: routing, permutation, h [T*k][d_ff] in wt, y_sorted
+ * [T*k][d] fp32, and for the block form the normalised input).  Returns 0
+ * for an invalid shape.  Host only. */
+size_t moe_workspace_size(const moe_shape* shape);
+
+/* Bytes of workspace moe_expert_ffn needs (h only).  Host only. */
+size_t moe_expert_ffn_workspace_size(const moe_shape* shape);
+
+/* Router: logits g = x W_g^T (+ bias), the k largest per token and their
+ * softmax weights.  ("Mixtral" page, "Прямой проход в формулах", MoE
+ * equation; "MoE изнутри" steps 1-2.)
+ *   x        [T][d] in act
+ *   w_gate   [E][d] fp32
+ *   bias     [E] fp32 or NULL (Mixtral has none; a Linear bias otherwise)
+ *   logits   [T][E] fp32 output or NULL
+ *   topk_idx [T][k] int32 output: slot 0 holds the larger logit; exactly
+ *            equal logits go to the lower expert index
+ *   topk_w   [T][k] fp32 output, sums to 1 per token                    */
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
+                     const float* bias, float* logits, int32_t* topk_idx,
+                     float* topk_w, void* stream);
+
+/* Dispatch: stable counting sort of the T*k (token, slot) pairs by expert,
+ * the order of the pages' `where(topk_idx == e)` loop ("Алгоритм").
+ *   topk_idx       [T][k] int32, entries in 0..E-1 (others are skipped and
+ *                  get inv_pos -1)
+ *   expert_offsets [E+1] int32 output: rows of expert e are
+ *                  [offsets[e], offsets[e+1]); empty experts get no rows
+ *   sorted_token   [T*k] int32 output: token of each row, ascending per expert
+ *   inv_pos        [T][k] int32 output: row holding (t, topk_idx[t][s])
+ *   ws, ws_bytes   unused, may be NULL / 0                                 */
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
+                        int32_t* expert_offsets, int32_t* sorted_token,
+                        int32_t* inv_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* Experts: for every row r of expert e (in dispatch order),
+ *   y_sorted[r] = (SiLU(x[t] W1_e^T) * (x[t] W3_e^T)) W2_e^T,  t = sorted_token[r]
+ * ("Прямой проход в формулах", MoE equation, the SwiGLU term).
+ *   x             [T][d] in act;  w1, w3 [E][d_ff][d], w2 [E][d][d_ff] in wt
+ *   y_sorted      [T*k][d] fp32 output
+ *   ws            >= moe_expert_ffn_workspace_size(shape) bytes
+ * Small T (<= 64, bf16) runs the weight-streaming path that reads each
+ * touched expert's weights once; larger T runs the grouped MFMA GEMM.       */
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
+                          const int32_t* expert_offsets, const int32_t* sorted_token,
+                          const void* w1, const void* w3, const void* w2,
+                          float* y_sorted, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: y[t] = sum_s topk_w[t][s] * y_sorted[inv_pos[t][s]] (+ residual[t]),
+ * in fp32, rounded once to act ("Алгоритм", the weighted index-add, done as
+ * a gather so no atomics are needed).
+ *   residual [T][d] in act or NULL; may alias y.  Rows with inv_pos < 0 are
+ *   skipped.                                                               */
+moe_status moe_combine(const moe_shape* shape, const float* y_sorted,
+                       const int32_t* inv_pos, const float* topk_w,
+                       const void* residual, void* y, void* stream);
+
+/* The whole layer: route -> dispatch -> experts -> combine on one stream.
+ *   y [T][d] in act output (must not alias x)
+ *   ws >= moe_workspace_size(shape) bytes                                   */
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate,
+                       const float* bias, const void* w1, const void* w3,
+                       const void* w2, void* y, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* One pre-norm residual MoE sublayer ("Прямой проход в формулах", block
+ * equation H = U + MoE(RMSNorm_2(U)); RMSNorm(z) = z / sqrt(mean z^2 + eps)
+ * * gamma), in place on h:
+ *   h_inout [T][d] in act, overwritten with h + MoE(RMSNorm(h))
+ *   gamma   [d] fp32;  eps > 0
+ * The router sees the fp32 normalised row; the experts see it rounded to act. */
+moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma,
+                             float eps, const float* w_gate, const float* bias,
+                             const void* w1, const void* w3, const void* w2,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Timing points.  After a successful call with MOE_TIMING_POINTS events,
+ * every moe_forward / moe_block_forward on the calling thread records
+ * events[i] on its stream at point i:
+ *   0 before the router   1 after the router   2 after dispatch
+ *   3 after the expert up kernel (h)   4 after the expert down kernel
+ *   5 after the combine
+ * so the elapsed time between consecutive points is one kernel's duration
+ * on that stream.  events are hipEvent_t handles created and owned by the
+ * caller; they must outlive their use.  count 0 or events NULL stops the
+ * recording.  Host only; thread-local.  MOE_ERR_INVALID_ARG for another
+ * count or a NULL handle. */
+#define MOE_TIMING_POINTS 6
+moe_status moe_set_timing_events(void* const* events, int32_t count);
+
+/* Message of the last non-OK status on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -16,7 +16,9 @@ listed in the pin tests (identity case, 28-pair brute force, fp64 shadow).
 from .moe_ref import (  # noqa: F401
     aux_loss_ref,
     block_forward_ref,
+    combine_ref,
     dispatch_ref,
+    expert_rows_ref,
     expert_swiglu,
     moe_forward_expert_loop,
     moe_forward_token_loop,

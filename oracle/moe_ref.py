@@ -199,6 +199,35 @@ def dispatch_ref(idx: np.ndarray, E: int):
     return offsets, sorted_token, inv_pos
 
 
+def combine_ref(y_sorted, inv_pos, topk_w, residual=None, dtype=np.float32) -> np.ndarray:
+    """Y[t] = sum_s w[t, s] * Expert_{idx[t,s]}(x_t), read back from the expert-sorted rows.
+
+    The index-add of [MIX-A] written as a gather: row inv_pos[t, s] of
+    y_sorted holds the output of token t's slot-s expert.  Slots are added in
+    order, starting from zero (or from the residual row when given).
+    """
+    T, k = inv_pos.shape
+    out = np.zeros((T, y_sorted.shape[1]), dtype=dtype)
+    for s in range(k):
+        out = out + topk_w[:, s:s + 1].astype(dtype) * y_sorted[inv_pos[:, s]].astype(dtype)
+    if residual is not None:
+        out = out + widen(residual, dtype)
+    return out
+
+
+def expert_rows_ref(x, sorted_token, offsets, w1, w3, w2, dtype=np.float32) -> np.ndarray:
+    """y_sorted[r] = Expert_e(x[sorted_token[r]]) for the rows of every expert e ([MIX-A], [MIX-F])."""
+    E = len(offsets) - 1
+    X = widen(x, dtype)
+    d = X.shape[1]
+    out = np.zeros((int(offsets[-1]), d), dtype=dtype)
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[lo:hi] = expert_swiglu(X[sorted_token[lo:hi]], w1[e], w3[e], w2[e], dtype)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # RMSNorm and the residual MoE sublayer  [MIX-F]
 # ----------------------------------------------------------------------------

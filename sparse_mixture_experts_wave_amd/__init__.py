@@ -1,0 +1,17 @@
+"""MI355X (gfx950) Mixtral sparse MoE feed-forward layer.
+
+y = sum_{i in Top2(x W_g)} softmax_i * (SiLU(x W1_i) * (x W3_i)) W2_i, computed by
+hand-written HIP kernels behind the C ABI in include/moe.h (libmoe.so).
+"""
+from ._lib import LIB_PATH, MoEError, load  # noqa: F401
+from .moe import (  # noqa: F401
+    expert_ffn_workspace_size,
+    make_shape,
+    moe_block_forward,
+    moe_combine,
+    moe_dispatch,
+    moe_expert_ffn,
+    moe_forward,
+    moe_route,
+    workspace_size,
+)

@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels.  Each returns the HIP status of
+// its launch(es); none synchronises.  Shapes are validated by the C ABI layer
+// (moe_api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router GEMM + top-2 + two-way softmax (optionally with a fused RMSNorm that
+// also writes the normalised rows u in the activation dtype).
+hipError_t launch_route(const void* x, bool x_bf16, const float* w_gate, const float* bias,
+                        float* logits, int32_t* topk_idx, float* topk_w, int64_t T, int d,
+                        int E, const float* gamma, float eps, void* u_out, hipStream_t stream);
+
+// Stable counting sort of (token, slot) pairs by expert.
+hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E,
+                           int32_t* expert_offsets, int32_t* sorted_token, int32_t* inv_pos,
+                           hipStream_t stream);
+
+// Expert SwiGLU FFN over the dispatched rows, bf16 weights/activations, in two
+// launches: up (h = SiLU(x W1^T) * (x W3^T), [T*k][d_ff] bf16) and down
+// (y_sorted = h W2^T, [T*k][d] fp32).  Small T streams the weights.
+hipError_t launch_expert_up_bf16(const uint16_t* x, const int32_t* expert_offsets,
+                                 const int32_t* sorted_token, const uint16_t* w1,
+                                 const uint16_t* w3, uint16_t* h, int64_t T, int k, int d,
+                                 int d_ff, int E, hipStream_t stream);
+hipError_t launch_expert_down_bf16(const uint16_t* h, const int32_t* expert_offsets,
+                                   const uint16_t* w2, float* y_sorted, int64_t T, int k, int d,
+                                   int d_ff, int E, hipStream_t stream);
+
+// Same in fp32 (h is [T*k][d_ff] fp32).
+hipError_t launch_expert_up_f32(const float* x, const int32_t* expert_offsets,
+                                const int32_t* sorted_token, const float* w1, const float* w3,
+                                float* h, int64_t T, int k, int d, int d_ff, int E,
+                                hipStream_t stream);
+hipError_t launch_expert_down_f32(const float* h, const int32_t* expert_offsets, const float* w2,
+                                  float* y_sorted, int64_t T, int k, int d, int d_ff, int E,
+                                  hipStream_t stream);
+
+// Weighted gather-combine (+ optional residual), output in the activation dtype.
+hipError_t launch_combine(const float* y_sorted, const int32_t* inv_pos, const float* topk_w,
+                          const void* residual, void* y, bool out_bf16, int64_t T, int k, int d,
+                          hipStream_t stream);
+
+// Token count at or below which the bf16 expert FFN streams weights
+// (decode regime) instead of running the tiled grouped GEMM.
+constexpr int64_t kStreamMaxT = 64;
+
+}  // namespace moe

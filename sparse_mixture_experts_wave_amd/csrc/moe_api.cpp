@@ -1,0 +1,321 @@
+// C ABI of the MoE layer: argument validation, workspace carving and the
+// launch sequence route -> dispatch -> experts -> combine.  Host code only;
+// every launch is asynchronous on the caller's stream and nothing here
+// synchronises or reads device memory.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int32_t dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+// Shape rules shared by every entry point.
+moe_status check_shape(const moe_shape* s) {
+  if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(s->T));
+  if (s->d <= 0 || s->d % 64 != 0 || s->d > 32768)
+    return fail(MOE_ERR_INVALID_ARG, "d = %d must be a positive multiple of 64, at most 32768", s->d);
+  if (s->d_ff <= 0 || s->d_ff % 64 != 0 || s->d_ff > 65536)
+    return fail(MOE_ERR_INVALID_ARG, "d_ff = %d must be a positive multiple of 64, at most 65536", s->d_ff);
+  if (s->E < 2 || s->E > 64) return fail(MOE_ERR_INVALID_ARG, "E = %d outside 2..64", s->E);
+  if (s->k < 1 || s->k > s->E)
+    return fail(MOE_ERR_INVALID_ARG, "top-k = %d outside 1..E (E = %d)", s->k, s->E);
+  if (s->act != MOE_F32 && s->act != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "act dtype %d unknown", s->act);
+  if (s->wt != MOE_F32 && s->wt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "wt dtype %d unknown", s->wt);
+  if (s->k != 2) return fail(MOE_ERR_UNSUPPORTED, "top-k = %d: only k = 2 is implemented", s->k);
+  if ((s->E & (s->E - 1)) != 0) return fail(MOE_ERR_UNSUPPORTED, "E = %d is not a power of two", s->E);
+  if (s->act != s->wt)
+    return fail(MOE_ERR_UNSUPPORTED, "dtype pair (act %d, wt %d): only (f32, f32) and (bf16, bf16)", s->act, s->wt);
+  // Row indices are int32 on the device.
+  if (s->T > (int64_t{1} << 30) / s->k)
+    return fail(MOE_ERR_INVALID_ARG, "T = %lld too large", static_cast<long long>(s->T));
+  return MOE_OK;
+}
+
+moe_status need(const void* p, const char* name) {
+  if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+moe_status optional(const void* p, const char* name) {
+  if (p != nullptr && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                 \
+  do {                                \
+    const moe_status st_ = (expr);    \
+    if (st_ != MOE_OK) return st_;    \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout of moe_forward / moe_block_forward.
+struct Layout {
+  size_t topk_idx, topk_w, offsets, sorted_token, inv_pos, h, y_sorted, u, total;
+};
+
+Layout layout(const moe_shape* s, bool block) {
+  const size_t rows = static_cast<size_t>(s->T) * s->k;
+  Layout L{};
+  size_t at = 0;
+  L.topk_idx = at; at += up(rows * 4);
+  L.topk_w = at; at += up(rows * 4);
+  L.offsets = at; at += up((s->E + 1) * 4);
+  L.sorted_token = at; at += up(rows * 4);
+  L.inv_pos = at; at += up(rows * 4);
+  L.h = at; at += up(rows * s->d_ff * esize(s->wt));
+  L.y_sorted = at; at += up(rows * s->d * 4);
+  L.u = at; if (block) at += up(static_cast<size_t>(s->T) * s->d * esize(s->act));
+  L.total = at;
+  return L;
+}
+
+size_t ffn_ws(const moe_shape* s) {
+  return up(static_cast<size_t>(s->T) * s->k * s->d_ff * esize(s->wt));
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+hipStream_t hs(void* stream) { return static_cast<hipStream_t>(stream); }
+
+moe_status run_route(const moe_shape* s, const void* x, const float* w_gate, const float* bias,
+                     float* logits, int32_t* idx, float* w, const float* gamma, float eps,
+                     void* u_out, void* stream) {
+  return hip_status(moe::launch_route(x, s->act == MOE_BF16, w_gate, bias, logits, idx, w, s->T, s->d,
+                                      s->E, gamma, eps, u_out, hs(stream)),
+                    "router launch");
+}
+
+// Optional per-thread timing points (moe_set_timing_events).
+thread_local hipEvent_t g_events[MOE_TIMING_POINTS];
+thread_local bool g_timing = false;
+
+moe_status mark(int point, void* stream) {
+  if (!g_timing) return MOE_OK;
+  return hip_status(hipEventRecord(g_events[point], hs(stream)), "timing event record");
+}
+
+moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const int32_t* st,
+                   const void* w1, const void* w3, const void* w2, float* y_sorted, void* h,
+                   void* stream, bool timed) {
+  hipError_t err;
+  if (s->wt == MOE_BF16) {
+    err = moe::launch_expert_up_bf16(static_cast<const uint16_t*>(x), off, st, static_cast<const uint16_t*>(w1),
+                                     static_cast<const uint16_t*>(w3), static_cast<uint16_t*>(h), s->T, s->k,
+                                     s->d, s->d_ff, s->E, hs(stream));
+  } else {
+    err = moe::launch_expert_up_f32(static_cast<const float*>(x), off, st, static_cast<const float*>(w1),
+                                    static_cast<const float*>(w3), static_cast<float*>(h), s->T, s->k, s->d,
+                                    s->d_ff, s->E, hs(stream));
+  }
+  MOE_TRY(hip_status(err, "expert up launch"));
+  if (timed) MOE_TRY(mark(3, stream));
+  if (s->wt == MOE_BF16) {
+    err = moe::launch_expert_down_bf16(static_cast<const uint16_t*>(h), off, static_cast<const uint16_t*>(w2),
+                                       y_sorted, s->T, s->k, s->d, s->d_ff, s->E, hs(stream));
+  } else {
+    err = moe::launch_expert_down_f32(static_cast<const float*>(h), off, static_cast<const float*>(w2), y_sorted,
+                                      s->T, s->k, s->d, s->d_ff, s->E, hs(stream));
+  }
+  return hip_status(err, "expert down launch");
+}
+
+moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, const float* bias,
+                        const void* w1, const void* w3, const void* w2, void* y, const void* residual,
+                        const float* gamma, float eps, void* ws, size_t ws_bytes, void* stream) {
+  const bool block = gamma != nullptr;
+  const Layout L = layout(s, block);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  int32_t* idx = at<int32_t>(ws, L.topk_idx);
+  float* w = at<float>(ws, L.topk_w);
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  int32_t* st = at<int32_t>(ws, L.sorted_token);
+  int32_t* inv = at<int32_t>(ws, L.inv_pos);
+  void* h = at<void>(ws, L.h);
+  float* ys = at<float>(ws, L.y_sorted);
+  const void* xin = x;
+  void* u = nullptr;
+  if (block) {
+    u = at<void>(ws, L.u);
+    xin = u;
+  }
+  MOE_TRY(mark(0, stream));
+  MOE_TRY(run_route(s, x, w_gate, bias, nullptr, idx, w, gamma, eps, u, stream));
+  MOE_TRY(mark(1, stream));
+  MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
+  MOE_TRY(mark(2, stream));
+  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, ys, h, stream, true));
+  MOE_TRY(mark(4, stream));
+  MOE_TRY(hip_status(moe::launch_combine(ys, inv, w, residual, y, s->act == MOE_BF16, s->T, s->k, s->d, hs(stream)),
+                     "combine launch"));
+  return mark(5, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return layout(shape, true).total;
+}
+
+size_t moe_expert_ffn_workspace_size(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return ffn_ws(shape);
+}
+
+moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                     float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(w_gate, "w_gate"));
+  MOE_TRY(optional(bias, "bias"));
+  MOE_TRY(optional(logits, "logits"));
+  MOE_TRY(need(topk_idx, "topk_idx"));
+  MOE_TRY(need(topk_w, "topk_w"));
+  return run_route(shape, x, w_gate, bias, logits, topk_idx, topk_w, nullptr, 0.f, nullptr, stream);
+}
+
+moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* expert_offsets,
+                        int32_t* sorted_token, int32_t* inv_pos, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  MOE_TRY(check_shape(shape));
+  MOE_TRY(need(expert_offsets, "expert_offsets"));
+  // With T == 0 the offsets are still defined (all zero), so the kernel runs;
+  // it touches no other buffer then.
+  if (shape->T > 0) {
+    MOE_TRY(need(topk_idx, "topk_idx"));
+    MOE_TRY(need(sorted_token, "sorted_token"));
+    MOE_TRY(need(inv_pos, "inv_pos"));
+  }
+  return hip_status(moe::launch_dispatch(topk_idx, shape->T, shape->k, shape->E, expert_offsets, sorted_token,
+                                         inv_pos, hs(stream)),
+                    "dispatch launch");
+}
+
+moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
+                          const int32_t* sorted_token, const void* w1, const void* w3, const void* w2,
+                          float* y_sorted, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(expert_offsets, "expert_offsets"));
+  MOE_TRY(need(sorted_token, "sorted_token"));
+  MOE_TRY(need(w1, "w1"));
+  MOE_TRY(need(w3, "w3"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(need(y_sorted, "y_sorted"));
+  MOE_TRY(need(ws, "ws"));
+  if (ws_bytes < ffn_ws(shape))
+    return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, ffn_ws(shape));
+  return run_ffn(shape, x, expert_offsets, sorted_token, w1, w3, w2, y_sorted, ws, stream, false);
+}
+
+moe_status moe_combine(const moe_shape* shape, const float* y_sorted, const int32_t* inv_pos,
+                       const float* topk_w, const void* residual, void* y, void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(y_sorted, "y_sorted"));
+  MOE_TRY(need(inv_pos, "inv_pos"));
+  MOE_TRY(need(topk_w, "topk_w"));
+  MOE_TRY(optional(residual, "residual"));
+  MOE_TRY(need(y, "y"));
+  return hip_status(moe::launch_combine(y_sorted, inv_pos, topk_w, residual, y, shape->act == MOE_BF16, shape->T,
+                                        shape->k, shape->d, hs(stream)),
+                    "combine launch");
+}
+
+moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                       const void* w1, const void* w3, const void* w2, void* y, void* ws, size_t ws_bytes,
+                       void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(w_gate, "w_gate"));
+  MOE_TRY(optional(bias, "bias"));
+  MOE_TRY(need(w1, "w1"));
+  MOE_TRY(need(w3, "w3"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(need(y, "y"));
+  if (x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
+  MOE_TRY(need(ws, "ws"));
+  return forward_impl(shape, x, w_gate, bias, w1, w3, w2, y, nullptr, nullptr, 0.f, ws, ws_bytes, stream);
+}
+
+moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma, float eps,
+                             const float* w_gate, const float* bias, const void* w1, const void* w3,
+                             const void* w2, void* ws, size_t ws_bytes, void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (!(eps > 0.f)) return fail(MOE_ERR_INVALID_ARG, "eps = %g must be > 0", static_cast<double>(eps));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(h_inout, "h_inout"));
+  MOE_TRY(need(gamma, "gamma"));
+  MOE_TRY(need(w_gate, "w_gate"));
+  MOE_TRY(optional(bias, "bias"));
+  MOE_TRY(need(w1, "w1"));
+  MOE_TRY(need(w3, "w3"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(need(ws, "ws"));
+  return forward_impl(shape, h_inout, w_gate, bias, w1, w3, w2, h_inout, h_inout, gamma, eps, ws, ws_bytes,
+                      stream);
+}
+
+moe_status moe_set_timing_events(void* const* events, int32_t count) {
+  if (events == nullptr || count == 0) {
+    g_timing = false;
+    return ok();
+  }
+  if (count != MOE_TIMING_POINTS)
+    return fail(MOE_ERR_INVALID_ARG, "count = %d, expected %d timing events", count, MOE_TIMING_POINTS);
+  for (int i = 0; i < MOE_TIMING_POINTS; ++i) {
+    if (events[i] == nullptr) return fail(MOE_ERR_INVALID_ARG, "timing event %d is NULL", i);
+    g_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_timing = true;
+  return ok();
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+// Router: g = x W_g^T (+ bias) in fp32, the two largest logits per token and
+// their two-way softmax.  ("Mixtral" textbook page, "Прямой проход в
+// формулах", MoE equation; "MoE изнутри", steps 1-2: Linear router, top-k,
+// softmax over the kept logits in float32.)
+//
+// One wavefront handles TPW tokens.  Each lane walks the row in 8-element
+// (16-byte bf16) chunks, so a wave reads 1 KiB of a row per step; every
+// router weight chunk it loads serves all TPW tokens.  The TPW x E partial
+// dot products are transposed through LDS so that lane j ends with the full
+// logit of (token j / E, expert j % E); the top-2 is then a butterfly over
+// the E lanes of each token (E is a power of two).
+//
+// With gamma != nullptr the kernel also applies RMSNorm: it accumulates
+// sum(x^2) next to the dot products, and since u = x * rinv * gamma the
+// logits are rinv * sum_j (x_j gamma_j) W[e][j]; the normalised rows u are
+// written (rounded to the activation dtype) for the experts.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <bool XBF16>
+__device__ __forceinline__ void load_x8(const void* x, int64_t off, float v[8]) {
+  if constexpr (XBF16) {
+    const u32x4 w = load16(static_cast<const uint16_t*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = lo_bf16(w[i]);
+      v[2 * i + 1] = hi_bf16(w[i]);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// (v, i) beats (w, j) when larger, or equal with the lower index.
+__device__ __forceinline__ bool beats(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+template <int E, int TPW, bool XBF16, bool NORM>
+__global__ __launch_bounds__(256) void router_top2_kernel(
+    const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    const float* __restrict__ gamma, float eps, void* __restrict__ u_out,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int T, int d) {
+  constexpr int P = TPW * E;            // partial sums per lane (<= 64)
+  constexpr int COLS = P + TPW;         // + sum of squares per token
+  constexpr int LD = COLS + 1;          // padded LDS row
+  __shared__ float red[4][64 * LD];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tok0 = (blockIdx.x * 4 + wave) * TPW;
+
+  float acc[TPW][E];
+  float ss[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    ss[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[t][e] = 0.f;
+  }
+
+  for (int base = 0; base < d; base += 512) {
+    const int col = base + lane * 8;
+    if (col < d) {
+      float xv[TPW][8];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (tok0 + t < T) {
+          load_x8<XBF16>(x, static_cast<int64_t>(tok0 + t) * d + col, xv[t]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[t][i] = 0.f;
+        }
+      }
+      if constexpr (NORM) {
+        const float4 g0 = *reinterpret_cast<const float4*>(gamma + col);
+        const float4 g1 = *reinterpret_cast<const float4*>(gamma + col + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ss[t] += xv[t][i] * xv[t][i];
+            xv[t][i] *= gv[i];
+          }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float4 w0 = *reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * d + col);
+        const float4 w1 = *reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * d + col + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[t][e] += xv[t][i] * wv[i];
+      }
+    }
+  }
+
+  // Transpose-reduce the partials through LDS.
+  float* r = red[wave];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[lane * LD + t * E + e] = acc[t][e];
+    r[lane * LD + P + t] = ss[t];
+  }
+  __syncthreads();
+  const int j = lane < P ? lane : P - 1;  // idle lanes mirror the last column
+  const int tl = j / E;
+  const int e = j % E;
+  float g = 0.f, sq = 0.f;
+  for (int l = 0; l < 64; ++l) {
+    g += r[l * LD + j];
+    if constexpr (NORM) sq += r[l * LD + P + tl];
+  }
+  float rinv = 1.f;
+  if constexpr (NORM) {
+    rinv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
+    g *= rinv;
+  }
+  if (bias != nullptr) g += bias[e];
+
+  const int tok = tok0 + tl;
+  const bool live = lane < P && tok < T;
+  if (live && logits != nullptr) logits[static_cast<int64_t>(tok) * E + e] = g;
+
+  // Top-2 over the E lanes of each token.
+  float v1 = g, v2 = -INFINITY;
+  int i1 = e, i2 = E;
+#pragma unroll
+  for (int m = E / 2; m >= 1; m >>= 1) {
+    const float ov1 = __shfl_xor(v1, m, 64);
+    const float ov2 = __shfl_xor(v2, m, 64);
+    const int oi1 = __shfl_xor(i1, m, 64);
+    const int oi2 = __shfl_xor(i2, m, 64);
+    float n1, n2;
+    int j1, j2;
+    if (beats(v1, i1, ov1, oi1)) {
+      n1 = v1; j1 = i1;
+      if (beats(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
+    } else {
+      n1 = ov1; j1 = oi1;
+      if (beats(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
+    }
+    v1 = n1; i1 = j1; v2 = n2; i2 = j2;
+  }
+  if (live && e == 0) {
+    const float q = expf(v2 - v1);
+    const float s = 1.0f + q;
+    topk_idx[2 * static_cast<int64_t>(tok)] = i1;
+    topk_idx[2 * static_cast<int64_t>(tok) + 1] = i2;
+    topk_w[2 * static_cast<int64_t>(tok)] = 1.0f / s;
+    topk_w[2 * static_cast<int64_t>(tok) + 1] = q / s;
+  }
+
+  if constexpr (NORM) {
+    // Write u = x * rinv * gamma for this wave's tokens.
+    for (int t = 0; t < TPW; ++t) {
+      const float rt = __shfl(rinv, t * E, 64);
+      if (tok0 + t >= T) break;
+      for (int base = 0; base < d; base += 512) {
+        const int col = base + lane * 8;
+        if (col >= d) break;
+        const int64_t off = static_cast<int64_t>(tok0 + t) * d + col;
+        float xv[8];
+        load_x8<XBF16>(x, off, xv);
+        const float4 g0 = *reinterpret_cast<const float4*>(gamma + col);
+        const float4 g1 = *reinterpret_cast<const float4*>(gamma + col + 4);
+        const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        if constexpr (XBF16) {
+          u32x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            o[i] = pack_bf16x2(xv[2 * i] * rt * gv[2 * i], xv[2 * i + 1] * rt * gv[2 * i + 1]);
+          store16(static_cast<uint16_t*>(u_out) + off, o);
+        } else {
+          float4* p = reinterpret_cast<float4*>(static_cast<float*>(u_out) + off);
+          p[0] = make_float4(xv[0] * rt * gv[0], xv[1] * rt * gv[1], xv[2] * rt * gv[2], xv[3] * rt * gv[3]);
+          p[1] = make_float4(xv[4] * rt * gv[4], xv[5] * rt * gv[5], xv[6] * rt * gv[6], xv[7] * rt * gv[7]);
+        }
+      }
+    }
+  }
+}
+
+template <int E, bool XBF16, bool NORM>
+hipError_t launch_e(const void* x, const float* wg, const float* bias, const float* gamma,
+                    float eps, void* u_out, float* logits, int32_t* idx, float* w, int64_t T,
+                    int d, hipStream_t s) {
+  constexpr int TPW = (64 / E) < 8 ? (64 / E) : 8;
+  const int64_t tokens_per_block = 4 * TPW;
+  const dim3 grid(static_cast<unsigned>((T + tokens_per_block - 1) / tokens_per_block));
+  router_top2_kernel<E, TPW, XBF16, NORM><<<grid, 256, 0, s>>>(
+      x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+  return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_dtype(const void* x, bool x_bf16, const float* wg, const float* bias,
+                        const float* gamma, float eps, void* u_out, float* logits, int32_t* idx,
+                        float* w, int64_t T, int d, hipStream_t s) {
+  if (x_bf16) {
+    return gamma ? launch_e<E, true, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s)
+                 : launch_e<E, true, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s);
+  }
+  return gamma ? launch_e<E, false, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s)
+               : launch_e<E, false, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s);
+}
+
+}  // namespace
+
+hipError_t launch_route(const void* x, bool x_bf16, const float* w_gate, const float* bias,
+                        float* logits, int32_t* topk_idx, float* topk_w, int64_t T, int d,
+                        int E, const float* gamma, float eps, void* u_out, hipStream_t stream) {
+  switch (E) {
+    case 2: return launch_dtype<2>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 4: return launch_dtype<4>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 8: return launch_dtype<8>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 16: return launch_dtype<16>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 32: return launch_dtype<32>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 64: return launch_dtype<64>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,166 @@
+"""Python binding of the MoE C ABI: same entry points, torch tensors in and out.
+
+Argument marshalling only.  torch allocates device memory and supplies the
+current HIP stream; every step of the layer runs in the HIP kernels of
+libmoe.so.  Tensors must be contiguous and on the GPU; bf16 data is passed
+as torch.bfloat16 (its bits are what the kernels read).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.MOE_F32, torch.bfloat16: _lib.MOE_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _gpu(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_shape(T: int, d: int, d_ff: int, E: int, k: int = 2,
+               act: torch.dtype = torch.bfloat16, wt: Optional[torch.dtype] = None) -> _lib.MoEShape:
+    wt = act if wt is None else wt
+    return _lib.MoEShape(int(T), int(d), int(d_ff), int(E), int(k), _DT.get(act, -1), _DT.get(wt, -1))
+
+
+def workspace_size(shape: _lib.MoEShape) -> int:
+    return int(_lib.load().moe_workspace_size(ctypes.byref(shape)))
+
+
+def expert_ffn_workspace_size(shape: _lib.MoEShape) -> int:
+    return int(_lib.load().moe_expert_ffn_workspace_size(ctypes.byref(shape)))
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# d_ff does not enter the router, dispatch or combine; any valid value does.
+_D_FF_UNUSED = 64
+
+
+def moe_route(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor] = None, k: int = 2,
+              want_logits: bool = False) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Router logits -> (topk_idx [T,k] int32, topk_w [T,k] fp32, logits [T,E] fp32 or None)."""
+    x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
+    T, d = x.shape
+    E = w_gate.shape[0]
+    if w_gate.dtype != torch.float32 or tuple(w_gate.shape) != (E, d):
+        raise ValueError("w_gate must be float32 [E, d]")
+    shape = make_shape(T, d, _D_FF_UNUSED, E, k, x.dtype)
+    idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device) if want_logits else None
+    _lib.check(_lib.load().moe_route(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(logits), _p(idx),
+                                     _p(w), _stream(x)))
+    return idx, w, logits
+
+
+def moe_dispatch(topk_idx: torch.Tensor, E: int, d: int = 64):
+    """-> (expert_offsets [E+1], sorted_token [T*k], inv_pos [T,k]) int32."""
+    topk_idx = _gpu(topk_idx, "topk_idx")
+    if topk_idx.dtype != torch.int32:
+        raise ValueError("topk_idx must be int32")
+    T, k = topk_idx.shape
+    shape = make_shape(T, d, _D_FF_UNUSED, E, k, torch.bfloat16)
+    dev = topk_idx.device
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    inv = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _lib.check(_lib.load().moe_dispatch(ctypes.byref(shape), _p(topk_idx), _p(off), _p(st), _p(inv), None, 0,
+                                        _stream(topk_idx)))
+    return off, st[:T * k], inv
+
+
+def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_token: torch.Tensor,
+                   w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, k: int = 2,
+                   y_sorted: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Expert SwiGLU on every dispatched row -> y_sorted [T*k, d] fp32."""
+    x, w1, w3, w2 = _gpu(x, "x"), _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
+    T, d = x.shape
+    E, d_ff, _ = w1.shape
+    if tuple(w1.shape) != (E, d_ff, d) or tuple(w3.shape) != (E, d_ff, d) or tuple(w2.shape) != (E, d, d_ff):
+        raise ValueError("expert weights must be w1, w3 [E, d_ff, d] and w2 [E, d, d_ff]")
+    shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
+    if y_sorted is None:
+        y_sorted = torch.empty((max(T * k, 1), d), dtype=torch.float32, device=x.device)
+    ws = _ws(expert_ffn_workspace_size(shape), x.device)
+    _lib.check(_lib.load().moe_expert_ffn(ctypes.byref(shape), _p(x), _p(expert_offsets), _p(sorted_token),
+                                          _p(w1), _p(w3), _p(w2), _p(y_sorted), _p(ws), ws.numel(),
+                                          _stream(x)))
+    return y_sorted[:T * k]
+
+
+def moe_combine(y_sorted: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Tensor, E: int,
+                out_dtype: torch.dtype = torch.bfloat16, residual: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[t] = sum_s w[t,s] * y_sorted[inv_pos[t,s]] (+ residual[t]) -> [T, d] in out_dtype."""
+    y_sorted, inv_pos, topk_w = _gpu(y_sorted, "y_sorted"), _gpu(inv_pos, "inv_pos"), _gpu(topk_w, "topk_w")
+    residual = _gpu(residual, "residual")
+    T, k = inv_pos.shape
+    d = y_sorted.shape[1]
+    shape = make_shape(T, d, _D_FF_UNUSED, E, k, out_dtype)
+    if out is None:
+        out = torch.empty((T, d), dtype=out_dtype, device=y_sorted.device)
+    _lib.check(_lib.load().moe_combine(ctypes.byref(shape), _p(y_sorted), _p(inv_pos), _p(topk_w), _p(residual),
+                                       _p(out), _stream(y_sorted)))
+    return out
+
+
+def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor], w1: torch.Tensor,
+                w3: torch.Tensor, w2: torch.Tensor, k: int = 2, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer y = sum_{i in Top2} softmax_i * SwiGLU_i(x) -> [T, d] in x.dtype."""
+    x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
+    w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
+    T, d = x.shape
+    E, d_ff, _ = w1.shape
+    shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = _ws(workspace_size(shape), x.device)
+    _lib.check(_lib.load().moe_forward(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2),
+                                       _p(out), _p(workspace), workspace.numel(), _stream(x)))
+    return out
+
+
+def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: torch.Tensor,
+                      bias: Optional[torch.Tensor], w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                      k: int = 2, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """In place: h <- h + MoE(RMSNorm(h) * gamma).  Returns h."""
+    h, gamma, w_gate, bias = _gpu(h, "h"), _gpu(gamma, "gamma"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
+    w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
+    T, d = h.shape
+    E, d_ff, _ = w1.shape
+    shape = make_shape(T, d, d_ff, E, k, h.dtype, w1.dtype)
+    if workspace is None:
+        workspace = _ws(workspace_size(shape), h.device)
+    _lib.check(_lib.load().moe_block_forward(ctypes.byref(shape), _p(h), _p(gamma), float(eps), _p(w_gate),
+                                             _p(bias), _p(w1), _p(w3), _p(w2), _p(workspace), workspace.numel(),
+                                             _stream(h)))
+    return h

@@ -1,0 +1,125 @@
+"""C ABI on the host: the library loads, exports every declared symbol, and
+validates arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_wave_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+# A 16-byte aligned address that is never dereferenced: every call below
+# fails validation (or returns for T == 0) before it could be used.
+FAKE = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(moe_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
+            "moe_block_forward", "moe_workspace_size", "moe_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def shape(T=16, d=4096, d_ff=14336, E=8, k=2, act=_lib.MOE_BF16, wt=None):
+    return _lib.MoEShape(T, d, d_ff, E, k, act, act if wt is None else wt)
+
+
+def route(lib, s, x=FAKE, wg=FAKE, idx=FAKE, w=FAKE):
+    return lib.moe_route(ctypes.byref(s), x, wg, None, None, idx, w, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d=100), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d_ff=96), _lib.MOE_ERR_INVALID_ARG),
+    (dict(E=1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(E=65), _lib.MOE_ERR_INVALID_ARG),
+    (dict(k=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(k=9), _lib.MOE_ERR_INVALID_ARG),      # k outside 1..E: the pages' ValueError
+    (dict(k=1), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(k=3), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(E=6), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(act=_lib.MOE_BF16, wt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(act=7), _lib.MOE_ERR_INVALID_ARG),
+])
+def test_shape_validation(lib, kw, status):
+    assert route(lib, shape(**kw)) == status
+    assert lib.moe_last_error().decode() != ""
+
+
+def test_null_and_misaligned_pointers(lib):
+    s = shape()
+    assert route(lib, s, x=None) == _lib.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in lib.moe_last_error()
+    assert route(lib, s, wg=MISALIGNED) == _lib.MOE_ERR_INVALID_ARG
+    assert b"aligned" in lib.moe_last_error()
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, MISALIGNED, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, FAKE, FAKE, None, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_zero_tokens_is_a_no_op(lib):
+    s = shape(T=0)
+    assert route(lib, s) == _lib.MOE_OK
+    assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None) == _lib.MOE_OK
+    assert lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x20000),
+                           None, 0, None) == _lib.MOE_OK
+    assert lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                              None) == _lib.MOE_OK
+
+
+def test_workspace_sizes(lib):
+    s = shape(T=4096)
+    rows = 4096 * 2
+    ws = lib.moe_workspace_size(ctypes.byref(s))
+    # h (bf16) + y_sorted (fp32) + normalised input dominate
+    assert ws >= rows * 14336 * 2 + rows * 4096 * 4 + 4096 * 4096 * 2
+    assert ws < rows * 14336 * 2 + rows * 4096 * 4 + 4096 * 4096 * 2 + (1 << 20)
+    assert lib.moe_expert_ffn_workspace_size(ctypes.byref(s)) == rows * 14336 * 2
+    assert lib.moe_workspace_size(ctypes.byref(shape(d=100))) == 0
+    assert lib.moe_workspace_size(None) == 0
+
+
+def test_workspace_too_small_is_rejected(lib):
+    s = shape(T=16)
+    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x20000),
+                         FAKE, 1024, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"workspace" in lib.moe_last_error()
+    st = lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_forward_rejects_aliased_output(lib):
+    s = shape(T=16)
+    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"alias" in lib.moe_last_error()
+
+
+def test_block_forward_validates_eps(lib):
+    s = shape(T=16)
+    st = lib.moe_block_forward(ctypes.byref(s), FAKE, FAKE, 0.0, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"eps" in lib.moe_last_error()
+
+
+def test_python_binding_maps_status_to_exceptions(lib):
+    with pytest.raises(ValueError):
+        _lib.check(route(lib, shape(d=100)))
+    with pytest.raises(NotImplementedError):
+        _lib.check(route(lib, shape(k=3)))
+    _lib.check(_lib.MOE_OK)

@@ -1,0 +1,336 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded
+inputs.  Small shapes span several tiles with ragged tails; the Mixtral shapes
+are checked in full where the oracle is quick, else on sampled tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_wave_amd as moe
+from synth import CONFIGS, generate, generate_torch
+
+from gpu_helpers import (BF16_TOL, F32_TOL, check_dispatch_on_clear, check_routing, clear_tokens,
+                         max_rel_err, say, to_dev, to_host, widen_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load()
+
+
+def small(name, T, d, d_ff, E=8, dtype="bf16", bias=None, cfg_id=10):
+    return CONFIGS["tiny_fp32"].with_(name=name, cfg_id=cfg_id, T=T, d=d, d_ff=d_ff, E=E, dtype=dtype,
+                                      bias=bias, x_unit_rms=False, wg_std=0.02)
+
+
+def run_forward(inp):
+    dv = {k: to_dev(v) for k, v in inp.items()}
+    y = moe.moe_forward(dv["x"], dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
+    torch.cuda.synchronize()
+    return to_host(y)
+
+
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,dtype,bias", [
+    (64, 128, 8, "f32", None),
+    (300, 192, 8, "bf16", None),
+    (1000, 512, 8, "bf16", "zipf1.2"),
+    (37, 256, 2, "bf16", None),
+    (77, 256, 4, "f32", None),
+    (129, 256, 16, "bf16", None),
+    (65, 256, 32, "f32", None),
+    (33, 256, 64, "bf16", None),
+    (1, 4096, 8, "bf16", None),
+])
+def test_router_parity(T, d, E, dtype, bias):
+    say(f"router T={T} d={d} E={E} {dtype} bias={bias}")
+    cfg = small("router", T, d, 64, E=E, dtype=dtype, bias=("zipf1.2" if bias else None))
+    inp = generate(cfg, tensors=("x", "w_gate"))
+    if E != 8 and bias:
+        inp["bias"] = None
+    g_ref, idx_ref, w_ref = oracle.route_ref(inp["x"], inp["w_gate"], inp["bias"])
+    idx, w, logits = moe.moe_route(to_dev(inp["x"]), to_dev(inp["w_gate"]), to_dev(inp["bias"]), want_logits=True)
+    torch.cuda.synchronize()
+    idx, w, logits = to_host(idx), to_host(w), to_host(logits)
+    np.testing.assert_allclose(logits, g_ref, rtol=1e-5, atol=1e-5)
+    check_routing(g_ref, idx_ref, w_ref, idx, w)
+
+
+def test_router_exact_ties_go_to_lower_index():
+    say("router ties")
+    cfg = small("ties", 200, 256, 64)
+    inp = generate(cfg, tensors=("x", "w_gate"))
+    wg = inp["w_gate"].copy()
+    wg[5] = wg[2]        # experts 2 and 5 always tie exactly
+    wg[7] = wg[2]
+    wg[2] += 0.5 * np.abs(wg[2])  # and make 2 (hence 5, 7) often win
+    wg[5] = wg[2]
+    wg[7] = wg[2]
+    idx, w, logits = moe.moe_route(to_dev(inp["x"]), to_dev(wg), None, want_logits=True)
+    torch.cuda.synchronize()
+    idx, logits = to_host(idx), to_host(logits)
+    assert np.array_equal(logits[:, 2], logits[:, 5]) and np.array_equal(logits[:, 2], logits[:, 7])
+    # wherever expert 2 is the best logit, the pair is (2, 5): ties go to the lower index
+    top = np.argmax(logits, axis=1)
+    sel = top == 2
+    assert sel.sum() > 10
+    assert np.all(idx[sel, 0] == 2) and np.all(idx[sel, 1] == 5)
+    assert not np.any(idx == 7)
+
+
+# ---------------------------------------------------------------------------
+# dispatch (integer work: bit-exact on identical inputs)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,E,mode", [
+    (1, 8, "random"), (16, 8, "random"), (1000, 8, "random"), (16384, 8, "zipf"),
+    (4097, 16, "random"), (500, 64, "random"), (300, 2, "random"), (2048, 8, "one_pair"),
+    (700, 8, "empty_experts"),
+])
+def test_dispatch_bit_exact(T, E, mode):
+    say(f"dispatch T={T} E={E} {mode}")
+    rng = np.random.default_rng(T * 131 + E)
+    g = rng.standard_normal((T, E)).astype(np.float32)
+    if mode == "zipf":
+        g += np.log(np.arange(1, E + 1, dtype=np.float32) ** -1.2)[None, :] * 3
+    if mode == "one_pair":
+        g[:, 3] += 100
+        g[:, 5] += 100
+    if mode == "empty_experts":
+        g[:, [0, 4, 6]] -= 100
+    idx = oracle.top2(g)
+    off_ref, st_ref, inv_ref = oracle.dispatch_ref(idx, E)
+    off, st, inv = moe.moe_dispatch(to_dev(idx), E)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(off), off_ref)
+    assert np.array_equal(to_host(st), st_ref)
+    assert np.array_equal(to_host(inv), inv_ref)
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,out_dtype,residual", [
+    (100, 256, torch.float32, False), (300, 192, torch.bfloat16, False), (257, 4096, torch.bfloat16, True),
+    (64, 128, torch.float32, True),
+])
+def test_combine(T, d, out_dtype, residual):
+    say(f"combine T={T} d={d} {out_dtype} residual={residual}")
+    rng = np.random.default_rng(T + d)
+    idx = oracle.top2(rng.standard_normal((T, 8)).astype(np.float32))
+    off, st, inv = oracle.dispatch_ref(idx, 8)
+    ys = rng.standard_normal((2 * T, d)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, 2)).astype(np.float32)
+    res = None
+    if residual:
+        res = rng.standard_normal((T, d)).astype(np.float32)
+        if out_dtype == torch.bfloat16:
+            from synth import bf16_bits_from_f32
+            res = bf16_bits_from_f32(res)
+    ref = oracle.combine_ref(ys, inv, w, res)
+    y = moe.moe_combine(to_dev(ys), to_dev(inv), to_dev(w), 8, out_dtype=out_dtype, residual=to_dev(res))
+    torch.cuda.synchronize()
+    y = widen_host(to_host(y))
+    if out_dtype == torch.bfloat16:
+        assert np.all(np.abs(y - ref) <= np.abs(ref) * 2 ** -8 + 1e-6)
+    else:
+        np.testing.assert_allclose(y, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_combine_residual_may_alias_output():
+    say("combine aliased residual")
+    T, d = 50, 256
+    rng = np.random.default_rng(1)
+    idx = oracle.top2(rng.standard_normal((T, 8)).astype(np.float32))
+    _, _, inv = oracle.dispatch_ref(idx, 8)
+    ys = rng.standard_normal((2 * T, d)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, 2)).astype(np.float32)
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    ref = oracle.combine_ref(ys, inv, w, h)
+    hd = to_dev(h)
+    moe.moe_combine(to_dev(ys), to_dev(inv), to_dev(w), 8, out_dtype=torch.float32, residual=hd, out=hd)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to_host(hd), ref, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# expert FFN (both bf16 paths and fp32)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,d_ff,dtype,path", [
+    (64, 128, 256, "f32", "gemm"),
+    (300, 192, 320, "bf16", "gemm"),
+    (1000, 256, 384, "bf16", "gemm"),
+    (5, 512, 1024, "bf16", "stream"),
+    (16, 512, 1536, "bf16", "stream"),
+    (30, 1024, 512, "bf16", "stream"),
+    (64, 512, 1024, "bf16", "stream"),
+    (16, 192, 256, "bf16", "gemm"),   # d not a multiple of 512: small T on the GEMM path
+])
+def test_expert_ffn(T, d, d_ff, dtype, path):
+    say(f"expert_ffn T={T} d={d} d_ff={d_ff} {dtype} {path}")
+    cfg = small("ffn", T, d, d_ff, dtype=dtype)
+    inp = generate(cfg)
+    g, idx, w = oracle.route_ref(inp["x"], inp["w_gate"], None)
+    off, st, inv = oracle.dispatch_ref(idx, 8)
+    ref = oracle.expert_rows_ref(inp["x"], st, off, inp["w1"], inp["w3"], inp["w2"])
+    ys = moe.moe_expert_ffn(to_dev(inp["x"]), to_dev(off), to_dev(st), to_dev(inp["w1"]), to_dev(inp["w3"]),
+                            to_dev(inp["w2"]))
+    torch.cuda.synchronize()
+    err = max_rel_err(to_host(ys), ref)
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL), err
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg", [
+    CONFIGS["tiny_fp32"],
+    small("small_bf16", 1000, 256, 384),
+    small("small_bf16_ragged", 300, 192, 320, bias="zipf1.2"),
+    small("small_decode", 16, 512, 1024),
+    small("small_decode40", 40, 512, 1024),
+    small("t1", 1, 256, 512),
+    small("t1_stream", 1, 512, 512),
+    small("small_fp32", 333, 192, 256, dtype="f32"),
+], ids=lambda c: c.name)
+def test_forward_small(cfg):
+    say(f"forward {cfg.name} T={cfg.T} d={cfg.d} d_ff={cfg.d_ff} {cfg.dtype}")
+    inp = generate(cfg)
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], inp["bias"], inp["w1"],
+                                                        inp["w3"], inp["w2"])
+    y = run_forward(inp)
+    clear, _ = clear_tokens(g)
+    err = max_rel_err(y, y_ref, clear)
+    assert err <= (F32_TOL if cfg.dtype == "f32" else BF16_TOL), err
+
+
+def test_forward_all_tokens_one_pair():
+    say("forward one pair")
+    cfg = small("one_pair", 500, 256, 384)
+    inp = generate(cfg)
+    inp["bias"] = np.zeros(8, np.float32)
+    inp["bias"][[3, 5]] = 50.0
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], inp["bias"], inp["w1"],
+                                                        inp["w3"], inp["w2"])
+    assert np.all(np.sort(idx, axis=1) == [3, 5])
+    y = run_forward(inp)
+    assert max_rel_err(y, y_ref) <= BF16_TOL
+
+
+def test_forward_identity_when_experts_equal():
+    # All experts equal: the layer is one dense SwiGLU whatever the routing,
+    # so near-tie tokens are checked too.
+    say("forward identity")
+    cfg = small("identity", 400, 256, 384)
+    inp = generate(cfg)
+    for key in ("w1", "w3", "w2"):
+        inp[key] = np.ascontiguousarray(np.broadcast_to(inp[key][0], inp[key].shape))
+    dense = oracle.expert_swiglu(inp["x"], inp["w1"][0], inp["w3"][0], inp["w2"][0])
+    y = run_forward(inp)
+    assert max_rel_err(y, dense) <= BF16_TOL
+
+
+def test_forward_zero_tokens():
+    say("forward T=0")
+    cfg = small("t0", 4, 256, 512)
+    inp = generate(cfg)
+    inp["x"] = inp["x"][:0]
+    dv = {k: to_dev(v) for k, v in inp.items()}
+    y = moe.moe_forward(dv["x"], dv["w_gate"], None, dv["w1"], dv["w3"], dv["w2"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, 256)
+
+
+def test_forward_is_deterministic():
+    say("forward determinism")
+    cfg = small("det", 777, 256, 384)
+    inp = generate(cfg)
+    a, b = run_forward(inp), run_forward(inp)
+    assert np.array_equal(a, b)
+
+
+def test_block_forward_two_layers_teacher_forced():
+    cfg = small("block", 300, 256, 384)
+    dv_h = None
+    for layer in range(2):
+        say(f"block layer {layer}")
+        inp = generate(cfg, layer=layer)
+        if dv_h is None:
+            dv_h = to_dev(inp["x"])
+        h_in = to_host(dv_h).copy()
+        gamma = np.linspace(0.5, 1.5, cfg.d).astype(np.float32)
+        moe.moe_block_forward(dv_h, to_dev(gamma), 1e-5, to_dev(inp["w_gate"]), None, to_dev(inp["w1"]),
+                              to_dev(inp["w3"]), to_dev(inp["w2"]))
+        torch.cuda.synchronize()
+        h_out = widen_host(to_host(dv_h))
+        ref, u, (g, idx, w) = oracle.block_forward_ref(h_in, gamma, 1e-5, inp["w_gate"], None, inp["w1"],
+                                                       inp["w3"], inp["w2"])
+        y_ref = ref - widen_host(h_in)
+        clear, _ = clear_tokens(g)
+        tol = BF16_TOL * np.max(np.abs(y_ref)) + 2 ** -8 * np.max(np.abs(ref))
+        assert np.max(np.abs(h_out[clear] - ref[clear])) <= tol
+
+
+# ---------------------------------------------------------------------------
+# Mixtral shapes
+# ---------------------------------------------------------------------------
+def _mixtral_case(name, sample):
+    cfg = CONFIGS[name]
+    say(f"mixtral {name}: generating")
+    dv = generate_torch(cfg, torch.device("cuda:0"))
+    x, wg, b = dv["x"], dv["w_gate"], dv["bias"]
+    say(f"mixtral {name}: route + dispatch + forward")
+    idx, w, _ = moe.moe_route(x, wg, b)
+    off, st, inv = moe.moe_dispatch(idx, cfg.E)
+    y = moe.moe_forward(x, wg, b, dv["w1"], dv["w3"], dv["w2"])
+    torch.cuda.synchronize()
+    say(f"mixtral {name}: oracle")
+    xh, wgh = to_host(x), to_host(wg)
+    bh = to_host(b) if b is not None else None
+    g_ref, idx_ref, w_ref = oracle.route_ref(xh, wgh, bh)
+    idx_h = to_host(idx)
+    clear = check_routing(g_ref, idx_ref, w_ref, idx_h, to_host(w))
+    check_dispatch_on_clear(idx_h, to_host(off), to_host(st), to_host(inv), clear, cfg.E)
+    # per expert, GPU rows minus near-tie tokens == oracle rows minus near-tie tokens
+    off_ref, st_ref, _ = oracle.dispatch_ref(idx_ref, cfg.E)
+    off_h, st_h = to_host(off), to_host(st)
+    for e in range(cfg.E):
+        a = [t for t in st_h[off_h[e]:off_h[e + 1]] if clear[t]]
+        r = [t for t in st_ref[off_ref[e]:off_ref[e + 1]] if clear[t]]
+        assert a == r, f"expert {e} rows differ"
+    counts = np.diff(off_h)
+    say(f"mixtral {name}: rows per expert {counts.tolist()}")
+    tokens = sample(cfg, counts, idx_h, clear)
+    w1, w3, w2 = to_host(dv["w1"]), to_host(dv["w3"]), to_host(dv["w2"])
+    y_ref, _ = oracle.moe_forward_tokens(xh[tokens], wgh, bh, w1, w3, w2)
+    err = max_rel_err(to_host(y)[tokens], y_ref)
+    say(f"mixtral {name}: max rel err {err:.3e} on {len(tokens)} tokens")
+    assert err <= BF16_TOL
+
+
+def _sample_tokens(cfg, counts, idx, clear, n=24):
+    rng = np.random.default_rng(7)
+    T = cfg.T
+    picks = set(rng.choice(T, size=min(n, T), replace=False).tolist())
+    picks.update([0, T - 1])
+    # tokens of the lightest and heaviest experts
+    for e in (int(np.argmin(counts)), int(np.argmax(counts))):
+        picks.update(np.nonzero(np.any(idx == e, axis=1))[0][-3:].tolist())
+    return np.array(sorted(t for t in picks if clear[t]), dtype=np.int64)
+
+
+def test_mixtral_decode_t16_full():
+    _mixtral_case("mixtral_decode_t16", lambda cfg, c, i, cl: np.nonzero(cl)[0])
+
+
+def test_mixtral_prefill_t4096_sampled():
+    _mixtral_case("mixtral_prefill_t4096", _sample_tokens)
+
+
+def test_mixtral_skewed_t16384_sampled():
+    _mixtral_case("mixtral_skewed_t16384", _sample_tokens)

@@ -396,3 +396,19 @@ def test_planted_mistake_is_caught(monkeypatch, name, target, mutant):
     ref, ok = _pair_bruteforce_torch(x, wg, None, w1, w3, w2)
     err = np.max(np.abs(y[ok] - ref[ok]))
     assert err > 1e-3 * np.max(np.abs(ref[ok])), name
+
+
+# ---------------------------------------------------------------------------
+# gather form of the combine == the pages' index-add form
+# ---------------------------------------------------------------------------
+def test_gather_combine_equals_index_add():
+    cfg = CONFIGS["tiny_fp32"]
+    inp = generate(cfg)
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], None, inp["w1"], inp["w3"],
+                                                        inp["w2"])
+    off, st, inv = oracle.dispatch_ref(idx, cfg.E)
+    rows = oracle.expert_rows_ref(inp["x"], st, off, inp["w1"], inp["w3"], inp["w2"])
+    y = oracle.combine_ref(rows, inv, w)
+    assert np.max(np.abs(y - y_ref)) <= 1e-6 * np.max(np.abs(y_ref))
+    res = np.ones_like(y)
+    np.testing.assert_allclose(oracle.combine_ref(rows, inv, w, res) - y, 1.0, atol=1e-5)
