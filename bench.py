@@ -236,6 +236,8 @@ def main():
     ap.add_argument("--secondary", default="mixtral_prefill_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration for HBM traffic)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (the layer is built and "
@@ -249,6 +251,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.copy_probe:
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.empty(n, dtype=torch.float32, device="cuda")
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+        return
     cfg = CONFIGS[a.config]
     res = measure(cfg, a.steps, a.warmup)
     prim = summarize(res)

@@ -1,0 +1,189 @@
+// Decode-regime expert FFN: few rows per expert, so the layer is bound by
+// reading the weights.  Every touched expert's W1/W3 (up) or W2 (down) is read
+// exactly once, straight from HBM into MFMA operands; experts with no rows are
+// skipped, so their weights are never read.  ("Mixtral" textbook page,
+// "Генерация": in generation only the selected experts run; "Прямой проход в
+// формулах": the expert term (SiLU(u W_gate) * u W_up) W_down.)
+//
+// Work item = (expert, 16*NG output columns).  A workgroup of KS waves takes
+// one item at a time (grid-stride over items); wave w covers the K range
+// [w K/KS, (w+1) K/KS) in 128-wide steps.  With v_mfma_f32_16x16x32_bf16,
+// lane (m = lane%16, q = lane/16) holds k-chunk q of each 32-wide step, so
+// each load instruction reads 64 contiguous bytes of 16 weight rows and the
+// four instructions of a step cover 256 contiguous bytes per row.  The
+// expert's rows (tokens) are the MFMA's A operand, 16 per M-block, MB blocks
+// per pass.  Partial sums of the KS waves are reduced through LDS by wave 0,
+// which applies the SiLU * up epilogue (up) or stores fp32 (down).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <int MB, int NG, int KS, bool GATED>
+__global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, void* __restrict__ out, int N, int K, int E) {
+  constexpr int NACC = MB * NG * (GATED ? 2 : 1);
+  __shared__ f32x4 red[KS - 1][NACC][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int m = lane & 15;
+  const int q = lane >> 4;
+  const int Kw = K / KS;
+  const int kb = wave * Kw;
+  const int tiles = N / (16 * NG);
+  const int items = E * tiles;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int e = item / tiles;
+    const int n0 = (item - e * tiles) * (16 * NG);
+    const int lo = offsets[e];
+    const int n_e = offsets[e + 1] - lo;
+    if (n_e <= 0) continue;  // untouched expert: its weights are not read
+
+    const uint16_t* b0row[NG];
+    const uint16_t* b1row[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int64_t n = static_cast<int64_t>(e) * N + n0 + 16 * g + m;
+      b0row[g] = B0 + n * K + kb + 8 * q;
+      b1row[g] = GATED ? B1 + n * K + kb + 8 * q : nullptr;
+    }
+
+    for (int rb = 0; rb < n_e; rb += 16 * MB) {
+      const uint16_t* arow[MB];
+      bool aok[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = rb + mb * 16 + m;
+        aok[mb] = r < n_e;
+        int src = 0;
+        if (aok[mb]) src = gather ? gather[lo + r] : lo + r;
+        arow[mb] = A + static_cast<int64_t>(src) * K + kb + 8 * q;
+      }
+      f32x4 acc0[MB][NG], acc1[MB][NG];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            acc0[mb][g][v] = 0.f;
+            acc1[mb][g][v] = 0.f;
+          }
+
+      for (int k = 0; k < Kw; k += 128) {
+        u32x4 w0[NG][4], w1[NG][4], xa[MB][4];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            w0[g][j] = load16(b0row[g] + k + 32 * j);
+            if constexpr (GATED) w1[g][j] = load16(b1row[g] + k + 32 * j);
+          }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xa[mb][j] = aok[mb] ? load16(arow[mb] + k + 32 * j) : zero;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+              acc0[mb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[mb][j]), as_bf16x8(w0[g][j]),
+                                                                    acc0[mb][g], 0, 0, 0);
+              if constexpr (GATED)
+                acc1[mb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[mb][j]),
+                                                                      as_bf16x8(w1[g][j]), acc1[mb][g], 0, 0, 0);
+            }
+      }
+
+      // Reduce the KS partial sums through LDS into wave 0.
+      if (wave > 0) {
+        int a = 0;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            red[wave - 1][a++][lane] = acc0[mb][g];
+            if constexpr (GATED) red[wave - 1][a++][lane] = acc1[mb][g];
+          }
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w) {
+          int a = 0;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+              acc0[mb][g] += red[w][a++][lane];
+              if constexpr (GATED) acc1[mb][g] += red[w][a++][lane];
+            }
+        }
+        // 16x16 accumulator layout: lane holds column lane%16, rows 4*(lane/16)+v.
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = rb + mb * 16 + 4 * q + v;
+              if (r < n_e) {
+                const int64_t o = static_cast<int64_t>(lo + r) * N + n0 + 16 * g + m;
+                if constexpr (GATED)
+                  static_cast<uint16_t*>(out)[o] = f32_to_bf16(silu_fast(acc0[mb][g][v]) * acc1[mb][g][v]);
+                else
+                  static_cast<float*>(out)[o] = acc0[mb][g][v];
+              }
+            }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+template <int MB, int NG, int KS, bool GATED>
+hipError_t launch_cfg(const uint16_t* A, const int32_t* gather, const int32_t* offsets,
+                      const uint16_t* B0, const uint16_t* B1, void* out, int N, int K, int E,
+                      int grid, hipStream_t s) {
+  const int items = E * (N / (16 * NG));
+  const int blocks = grid > 0 && grid < items ? grid : items;
+  stream_ffn_bf16_kernel<MB, NG, KS, GATED><<<blocks, 64 * KS, 0, s>>>(A, gather, offsets, B0, B1, out, N, K, E);
+  return hipGetLastError();
+}
+
+template <int NG, int KS, bool GATED>
+hipError_t launch_mb(int64_t T, const uint16_t* A, const int32_t* gather, const int32_t* offsets,
+                     const uint16_t* B0, const uint16_t* B1, void* out, int N, int K, int E, int grid,
+                     hipStream_t s) {
+  // n_e <= T: the experts of one token are distinct.
+  if (T <= 16) return launch_cfg<1, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
+  if (T <= 32) return launch_cfg<2, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
+  return launch_cfg<4, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
+}
+
+}  // namespace
+
+bool stream_supported(int64_t T, int d, int d_ff) {
+  return T <= kStreamMaxT && d % 512 == 0 && d_ff % 512 == 0;
+}
+
+hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
+                                 const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
+                                 int d_ff, int E, hipStream_t stream) {
+  return launch_mb<2, 4, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, 0, stream);
+}
+
+hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2, float* y_sorted,
+                                   int64_t T, int d, int d_ff, int E, hipStream_t stream) {
+  return launch_mb<2, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, 0, stream);
+}
+
+}  // namespace moe

@@ -44,6 +44,24 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* inv_pos, const f
                           const void* residual, void* y, bool out_bf16, int64_t T, int k, int d,
                           hipStream_t stream);
 
+// Decode-regime streaming kernels (expert_stream.hip), used by the bf16
+// launchers above when stream_supported(T, d, d_ff).
+bool stream_supported(int64_t T, int d, int d_ff);
+hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
+                                 const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
+                                 int d_ff, int E, hipStream_t stream);
+hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
+                                   float* y_sorted, int64_t T, int d, int d_ff, int E,
+                                   hipStream_t stream);
+
+// Prefill-regime grouped MFMA GEMMs (expert_gemm.hip).
+hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
+                               const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int k,
+                               int d, int d_ff, int E, hipStream_t stream);
+hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
+                                 float* y_sorted, int64_t T, int k, int d, int d_ff, int E,
+                                 hipStream_t stream);
+
 // Token count at or below which the bf16 expert FFN streams weights
 // (decode regime) instead of running the tiled grouped GEMM.
 constexpr int64_t kStreamMaxT = 64;

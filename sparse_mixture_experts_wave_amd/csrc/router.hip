@@ -3,17 +3,20 @@
 // формулах", MoE equation; "MoE изнутри", steps 1-2: Linear router, top-k,
 // softmax over the kept logits in float32.)
 //
-// One wavefront handles TPW tokens.  Each lane walks the row in 8-element
-// (16-byte bf16) chunks, so a wave reads 1 KiB of a row per step; every
-// router weight chunk it loads serves all TPW tokens.  The TPW x E partial
-// dot products are transposed through LDS so that lane j ends with the full
-// logit of (token j / E, expert j % E); the top-2 is then a butterfly over
-// the E lanes of each token (E is a power of two).
+// A workgroup handles TPB tokens; its four waves split the row into
+// quarters.  Each lane walks its quarter in 8-element (16-byte bf16) chunks,
+// so a wave reads 1 KiB of a row per step, and every router weight chunk it
+// loads serves all TPB tokens.  The TPB x E partial dot products are
+// transposed through LDS: lane j of each wave sums column j over its 64
+// lanes, then wave 0 adds the four quarters, so lane j ends with the logit
+// of (token j / E, expert j % E).  The top-2 is a butterfly over the E lanes
+// of each token (E is a power of two).  Small T uses one token per workgroup
+// so that T workgroups share the work.
 //
 // With gamma != nullptr the kernel also applies RMSNorm: it accumulates
 // sum(x^2) next to the dot products, and since u = x * rinv * gamma the
 // logits are rinv * sum_j (x_j gamma_j) W[e][j]; the normalised rows u are
-// written (rounded to the activation dtype) for the experts.
+// then written (rounded to the activation dtype) for the experts.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,36 +45,41 @@ __device__ __forceinline__ bool beats(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
 
-template <int E, int TPW, bool XBF16, bool NORM>
+template <int E, int TPB, bool XBF16, bool NORM>
 __global__ __launch_bounds__(256) void router_top2_kernel(
     const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     const float* __restrict__ gamma, float eps, void* __restrict__ u_out,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int T, int d) {
-  constexpr int P = TPW * E;            // partial sums per lane (<= 64)
-  constexpr int COLS = P + TPW;         // + sum of squares per token
-  constexpr int LD = COLS + 1;          // padded LDS row
+  constexpr int P = TPB * E;                   // logits per workgroup (<= 64)
+  constexpr int COLS = P + (NORM ? TPB : 0);   // + sum of squares per token
+  constexpr int LD = COLS + 1;                 // padded LDS row
   __shared__ float red[4][64 * LD];
+  __shared__ float part[4][COLS];
+  __shared__ float rinv_s[TPB];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tok0 = (blockIdx.x * 4 + wave) * TPW;
+  const int tok0 = blockIdx.x * TPB;
+  const int quarter = d >> 2;  // a multiple of 16
+  const int cbeg = wave * quarter;
+  const int cend = cbeg + quarter;
 
-  float acc[TPW][E];
-  float ss[TPW];
+  float acc[TPB][E];
+  float ss[TPB];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < TPB; ++t) {
     ss[t] = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[t][e] = 0.f;
   }
 
-  for (int base = 0; base < d; base += 512) {
+  for (int base = cbeg; base < cend; base += 512) {
     const int col = base + lane * 8;
-    if (col < d) {
-      float xv[TPW][8];
+    if (col < cend) {
+      float xv[TPB][8];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
+      for (int t = 0; t < TPB; ++t) {
         if (tok0 + t < T) {
           load_x8<XBF16>(x, static_cast<int64_t>(tok0 + t) * d + col, xv[t]);
         } else {
@@ -84,7 +92,7 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
         const float4 g1 = *reinterpret_cast<const float4*>(gamma + col + 4);
         const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TPB; ++t)
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             ss[t] += xv[t][i] * xv[t][i];
@@ -97,78 +105,82 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
         const float4 w1 = *reinterpret_cast<const float4*>(wg + static_cast<int64_t>(e) * d + col + 4);
         const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TPB; ++t)
 #pragma unroll
           for (int i = 0; i < 8; ++i) acc[t][e] += xv[t][i] * wv[i];
       }
     }
   }
 
-  // Transpose-reduce the partials through LDS.
+  // Column sums over the 64 lanes of each wave, then over the four waves.
   float* r = red[wave];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  for (int t = 0; t < TPB; ++t) {
 #pragma unroll
     for (int e = 0; e < E; ++e) r[lane * LD + t * E + e] = acc[t][e];
-    r[lane * LD + P + t] = ss[t];
+    if constexpr (NORM) r[lane * LD + P + t] = ss[t];
   }
   __syncthreads();
-  const int j = lane < P ? lane : P - 1;  // idle lanes mirror the last column
-  const int tl = j / E;
-  const int e = j % E;
-  float g = 0.f, sq = 0.f;
-  for (int l = 0; l < 64; ++l) {
-    g += r[l * LD + j];
-    if constexpr (NORM) sq += r[l * LD + P + tl];
+  if (lane < COLS) {
+    float s = 0.f;
+    for (int l = 0; l < 64; ++l) s += r[l * LD + lane];
+    part[wave][lane] = s;
   }
-  float rinv = 1.f;
-  if constexpr (NORM) {
-    rinv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
-    g *= rinv;
-  }
-  if (bias != nullptr) g += bias[e];
+  __syncthreads();
 
-  const int tok = tok0 + tl;
-  const bool live = lane < P && tok < T;
-  if (live && logits != nullptr) logits[static_cast<int64_t>(tok) * E + e] = g;
-
-  // Top-2 over the E lanes of each token.
-  float v1 = g, v2 = -INFINITY;
-  int i1 = e, i2 = E;
-#pragma unroll
-  for (int m = E / 2; m >= 1; m >>= 1) {
-    const float ov1 = __shfl_xor(v1, m, 64);
-    const float ov2 = __shfl_xor(v2, m, 64);
-    const int oi1 = __shfl_xor(i1, m, 64);
-    const int oi2 = __shfl_xor(i2, m, 64);
-    float n1, n2;
-    int j1, j2;
-    if (beats(v1, i1, ov1, oi1)) {
-      n1 = v1; j1 = i1;
-      if (beats(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
-    } else {
-      n1 = ov1; j1 = oi1;
-      if (beats(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
+  if (wave == 0) {
+    const int j = lane < P ? lane : P - 1;  // idle lanes mirror the last column
+    const int tl = j / E;
+    const int e = j % E;
+    float g = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    if constexpr (NORM) {
+      const float sq = part[0][P + tl] + part[1][P + tl] + part[2][P + tl] + part[3][P + tl];
+      const float rinv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
+      g *= rinv;
+      if (lane < P && e == 0) rinv_s[tl] = rinv;
     }
-    v1 = n1; i1 = j1; v2 = n2; i2 = j2;
-  }
-  if (live && e == 0) {
-    const float q = expf(v2 - v1);
-    const float s = 1.0f + q;
-    topk_idx[2 * static_cast<int64_t>(tok)] = i1;
-    topk_idx[2 * static_cast<int64_t>(tok) + 1] = i2;
-    topk_w[2 * static_cast<int64_t>(tok)] = 1.0f / s;
-    topk_w[2 * static_cast<int64_t>(tok) + 1] = q / s;
+    if (bias != nullptr) g += bias[e];
+
+    const int tok = tok0 + tl;
+    const bool live = lane < P && tok < T;
+    if (live && logits != nullptr) logits[static_cast<int64_t>(tok) * E + e] = g;
+
+    // Top-2 over the E lanes of each token.
+    float v1 = g, v2 = -INFINITY;
+    int i1 = e, i2 = E;
+#pragma unroll
+    for (int m = E / 2; m >= 1; m >>= 1) {
+      const float ov1 = __shfl_xor(v1, m, 64);
+      const float ov2 = __shfl_xor(v2, m, 64);
+      const int oi1 = __shfl_xor(i1, m, 64);
+      const int oi2 = __shfl_xor(i2, m, 64);
+      float n1, n2;
+      int j1, j2;
+      if (beats(v1, i1, ov1, oi1)) {
+        n1 = v1; j1 = i1;
+        if (beats(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
+      } else {
+        n1 = ov1; j1 = oi1;
+        if (beats(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
+      }
+      v1 = n1; i1 = j1; v2 = n2; i2 = j2;
+    }
+    if (live && e == 0) {
+      const float q = expf(v2 - v1);
+      const float s = 1.0f + q;
+      topk_idx[2 * static_cast<int64_t>(tok)] = i1;
+      topk_idx[2 * static_cast<int64_t>(tok) + 1] = i2;
+      topk_w[2 * static_cast<int64_t>(tok)] = 1.0f / s;
+      topk_w[2 * static_cast<int64_t>(tok) + 1] = q / s;
+    }
   }
 
   if constexpr (NORM) {
-    // Write u = x * rinv * gamma for this wave's tokens.
-    for (int t = 0; t < TPW; ++t) {
-      const float rt = __shfl(rinv, t * E, 64);
-      if (tok0 + t >= T) break;
-      for (int base = 0; base < d; base += 512) {
-        const int col = base + lane * 8;
-        if (col >= d) break;
+    // u = x * rinv * gamma for the workgroup's tokens, 8 columns per thread.
+    __syncthreads();
+    for (int t = 0; t < TPB && tok0 + t < T; ++t) {
+      const float rt = rinv_s[t];
+      for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
         const int64_t off = static_cast<int64_t>(tok0 + t) * d + col;
         float xv[8];
         load_x8<XBF16>(x, off, xv);
@@ -191,15 +203,23 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
   }
 }
 
+// Small T: one token per workgroup (T workgroups); large T: as many tokens
+// per workgroup as fit 64 logits (at most 8), so router weights are reused.
+constexpr int64_t kRouterOneTokenMaxT = 2048;
+
 template <int E, bool XBF16, bool NORM>
 hipError_t launch_e(const void* x, const float* wg, const float* bias, const float* gamma,
                     float eps, void* u_out, float* logits, int32_t* idx, float* w, int64_t T,
                     int d, hipStream_t s) {
-  constexpr int TPW = (64 / E) < 8 ? (64 / E) : 8;
-  const int64_t tokens_per_block = 4 * TPW;
-  const dim3 grid(static_cast<unsigned>((T + tokens_per_block - 1) / tokens_per_block));
-  router_top2_kernel<E, TPW, XBF16, NORM><<<grid, 256, 0, s>>>(
-      x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+  constexpr int TPB = (64 / E) < 8 ? (64 / E) : 8;
+  if (T <= kRouterOneTokenMaxT) {
+    router_top2_kernel<E, 1, XBF16, NORM><<<static_cast<unsigned>(T), 256, 0, s>>>(
+        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+  } else {
+    const dim3 grid(static_cast<unsigned>((T + TPB - 1) / TPB));
+    router_top2_kernel<E, TPB, XBF16, NORM><<<grid, 256, 0, s>>>(
+        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+  }
   return hipGetLastError();
 }
 

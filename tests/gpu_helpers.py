@@ -47,6 +47,8 @@ def widen_host(a):
 
 def clear_tokens(g_ref, gap=GAP):
     s = np.sort(g_ref.astype(np.float64), axis=1)[:, ::-1]
+    if s.shape[1] == 2:  # k == E: every expert is selected, the set is never in doubt
+        s = np.concatenate([s, np.full((s.shape[0], 1), -np.inf)], axis=1)
     clear = (s[:, 1] - s[:, 2]) > gap
     ordered = clear & ((s[:, 0] - s[:, 1]) > gap)
     return clear, ordered
