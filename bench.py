@@ -35,10 +35,22 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 KERNELS = ["router", "dispatch", "expert_up", "expert_down", "combine"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "router": "router.hip", "dispatch": "dispatch.hip", "expert_up": "expert_ffn.hip",
-    "expert_down": "expert_ffn.hip", "combine": "combine.hip",
-}
+COPY_PROBE_BYTES = 1 << 30
+
+
+def kernel_source(kernel: str, T: int) -> str:
+    """Source file of the kernel that runs as `kernel` at T tokens (bf16)."""
+    if kernel in ("expert_up", "expert_down"):
+        return "expert_stream.hip" if T <= 64 else "expert_gemm.hip"
+    return {"router": "router.hip", "dispatch": "dispatch.hip", "combine": "combine.hip"}[kernel]
+
+
+# rocprofv3 kernel names -> step names
+KERNEL_PATTERNS = [
+    (r"stream_ffn_bf16_kernel<.*true>", "expert_up"), (r"stream_ffn_bf16_kernel<.*false>", "expert_down"),
+    (r"gemm_bf16_kernel<true>", "expert_up"), (r"gemm_bf16_kernel<false>", "expert_down"),
+    (r"router_top2_kernel", "router"), (r"dispatch_kernel", "dispatch"), (r"combine_kernel", "combine"),
+]
 
 
 def _hip():
@@ -66,16 +78,69 @@ def _src_sha(name: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _traffic(workload: str, kernel: str):
+def _traffic(workload: str, kernel: str, T: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
     absent or taken on a different version of the kernel's source."""
     try:
         entry = json.load(open(TRAFFIC_FILE))[workload][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if entry.get("src_sha") != _src_sha(KERNEL_SOURCES[kernel]):
+    if entry.get("src_sha") != _src_sha(kernel_source(kernel, T)):
         return None
     return entry.get("bytes_per_launch")
+
+
+def _counter_avgs(path: str):
+    """Average counter value per (step name, counter) over the MoE kernels of a
+    rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    sums = {}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        for pat, step in KERNEL_PATTERNS:
+            if re.search(pat, name):
+                key = (step, r["Counter_Name"])
+                tot, n = sums.get(key, (0.0, 0))
+                sums[key] = (tot + float(r["Counter_Value"]), n + 1)
+                break
+    return {k: tot / n for k, (tot, n) in sums.items()}
+
+
+def _copy_kib(path: str, counter: str) -> float:
+    import csv
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]:
+            return float(r["Counter_Value"])
+    raise SystemExit(f"no copy kernel with {counter} in {path}")
+
+
+def traffic_from(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
+    """Write profiles/traffic.json entries for `workload` from two rocprofv3
+    --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) of the bench and of
+    the copy probe (1 GiB read + 1 GiB written, which calibrates each counter)."""
+    from synth import CONFIGS
+    cfg = CONFIGS[workload]
+    f_scale = COPY_PROBE_BYTES / (_copy_kib(copy_fetch_csv, "FETCH_SIZE") * 1024)
+    w_scale = COPY_PROBE_BYTES / (_copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
+    fetch, write = _counter_avgs(fetch_csv), _counter_avgs(write_csv)
+    try:
+        out = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        out = {}
+    entries = {}
+    for step in KERNELS:
+        if (step, "FETCH_SIZE") not in fetch or (step, "WRITE_SIZE") not in write:
+            continue
+        rb = fetch[(step, "FETCH_SIZE")] * 1024 * f_scale
+        wb = write[(step, "WRITE_SIZE")] * 1024 * w_scale
+        entries[step] = {"bytes_per_launch": round(rb + wb), "read_bytes": round(rb), "write_bytes": round(wb),
+                         "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                         "src_sha": _src_sha(kernel_source(step, cfg.T))}
+    out[workload] = entries
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    print(json.dumps({workload: entries}, indent=1))
 
 
 def work_model(cfg, counts):
@@ -123,15 +188,17 @@ def measure(cfg, steps: int, warmup: int):
         step()
     torch.cuda.synchronize()
 
-    # Plain timed region (no per-kernel events).
+    # Timed region 1: K steps exactly as a caller runs them -> value.
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
     plain_ms = (time.perf_counter() - t0) * 1e3 / steps
 
-    # Timed region with the C ABI timing points on the launch stream.
-    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    # Timed region 2: the same K steps with the C ABI timing points recording
+    # HIP events on the launch stream between kernels -> per-kernel durations.
     evs = [[_event(hip) for _ in range(_lib.MOE_TIMING_POINTS)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -155,8 +222,8 @@ def measure(cfg, steps: int, warmup: int):
     counts = np.diff(off.cpu().numpy()).tolist()
     work = work_model(cfg, counts)
     return {
-        "cfg": cfg, "inputs": dv, "y": y, "ms_per_step": wall_ms, "ms_per_step_events": statistics.fmean(step_ms),
-        "ms_per_step_plain": plain_ms, "per_kernel_ms": per_kernel, "counts": counts, "work": work,
+        "cfg": cfg, "inputs": dv, "y": y, "ms_per_step": plain_ms, "ms_per_step_events": statistics.fmean(step_ms),
+        "ms_per_step_with_events": wall_ms, "per_kernel_ms": per_kernel, "counts": counts, "work": work,
     }
 
 
@@ -172,11 +239,11 @@ def roofline(res):
         peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
         unit, bound = "TFLOP/s", "mfma"
     return {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom),
+            "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom, cfg.T),
             "kernel_ms": round(pk[dom], 4)}
 
 
-def cpu_baseline(res, max_tokens: int):
+def cpu_baseline(res, max_tokens: int, budget_s: float = 10.0):
     """The CPU oracle (expert-loop form, numpy fp32) on a bounded sample of the
     same workload, on this host's cores: tokens/s."""
     import numpy as np
@@ -203,14 +270,15 @@ def cpu_baseline(res, max_tokens: int):
     print(f"[bench] cpu oracle on {n} tokens of {cfg.name}", file=sys.stderr, flush=True)
     oracle.moe_forward_expert_loop(*args)  # warm-up
     times = []
-    for _ in range(3):
+    start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - start < budget_s and len(times) < 50):
         t0 = time.perf_counter()
         oracle.moe_forward_expert_loop(*args)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": round(n / med, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} tokens of {cfg.name} (numpy fp32 expert-loop oracle, weights widened from bf16 "
-                      f"inside), 1 warm-up + 3 timed, median {med:.2f} s"}
+                      f"inside), 1 warm-up + {len(times)} timed runs ({sum(times):.1f} s), median {med:.3f} s"}
 
 
 def summarize(res):
@@ -223,7 +291,7 @@ def summarize(res):
         "roofline": roofline(res),
         "per_kernel_ms": {k: round(v, 4) for k, v in res["per_kernel_ms"].items()},
         "rows_per_expert": res["counts"], "touched_experts": work["touched_experts"],
-        "ms_per_step_without_timing_events": round(res["ms_per_step_plain"], 4),
+        "ms_per_step_with_timing_events": round(res["ms_per_step_with_events"], 4),
     }
 
 
@@ -236,9 +304,14 @@ def main():
     ap.add_argument("--secondary", default="mixtral_prefill_t4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write profiles/traffic.json for --config from rocprofv3 --pmc CSVs (no GPU needed)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for HBM traffic)")
     a = ap.parse_args()
+    if a.traffic_from:
+        traffic_from(a.config, *a.traffic_from)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} is not supported (the layer is built and "
               "measured on a single MI355X; multi-GPU sharding is a design note, not a run)", file=sys.stderr)
