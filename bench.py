@@ -5,12 +5,13 @@ One step = one full layer forward (router + top-2 softmax, dispatch, expert
 SwiGLU up/down, weighted combine) through the C ABI's moe_forward on inputs
 already resident in HBM.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME] [--secondary NAME|none]
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--secondary A,B,..|none]
                     [--no-cpu-baseline]
 
 The default workload is the Mixtral 8x7B layer in the decode regime (T = 16,
-HBM-bound); the prefill layer (T = 4096, MFMA-bound) is measured too and
-reported under "secondary".  Per-kernel durations come from HIP events that
+HBM-bound); the prefill layer (T = 4096), the Zipf-skewed layer (T = 16384)
+and the 32-layer residual stack (T = 2048, one step = all 32 sublayers) are
+measured too and reported under "secondary".  Per-kernel durations come from HIP events that
 moe_forward records on its own stream between its kernels (timing points of
 the C ABI); the roofline fraction is that of the dominant kernel.
 """
@@ -164,6 +165,8 @@ def work_model(cfg, counts):
 
 
 def measure(cfg, steps: int, warmup: int):
+    """Time `steps` steps of the workload: one moe_forward call, or for a stack
+    workload one moe_block_forward call per layer on a resident residual stream."""
     import numpy as np
     import torch
 
@@ -174,15 +177,27 @@ def measure(cfg, steps: int, warmup: int):
     lib = moe.load()
     hip = _hip()
     dev = torch.device("cuda:0")
-    print(f"[bench] {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    dv = generate_torch(cfg, dev)
-    shape = moe.make_shape(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, dv["x"].dtype)
+    print(f"[bench] {cfg.name}: generating inputs ({cfg.layers} layer(s))", file=sys.stderr, flush=True)
+    layers = [generate_torch(cfg, dev, layer=l) for l in range(cfg.layers)]
+    x = layers[0]["x"]
+    for lw in layers[1:]:
+        del lw["x"]
+    shape = moe.make_shape(cfg.T, cfg.d, cfg.d_ff, cfg.E, cfg.k, x.dtype)
     ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(dv["x"])
-    args = (dv["x"], dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
+    stack = cfg.layers > 1
+    gamma = torch.ones(cfg.d, dtype=torch.float32, device=dev)
+    y = x.clone() if stack else torch.empty_like(x)  # the stack's residual stream, updated in place
+
+    def call(lw):
+        if stack:
+            moe.moe_block_forward(y, gamma, 1e-5, lw["w_gate"], lw["bias"], lw["w1"], lw["w3"], lw["w2"],
+                                  workspace=ws)
+        else:
+            moe.moe_forward(x, lw["w_gate"], lw["bias"], lw["w1"], lw["w3"], lw["w2"], out=y, workspace=ws)
 
     def step():
-        moe.moe_forward(*args, out=y, workspace=ws)
+        for lw in layers:
+            call(lw)
 
     for _ in range(warmup):
         step()
@@ -199,30 +214,32 @@ def measure(cfg, steps: int, warmup: int):
 
     # Timed region 2: the same K steps with the C ABI timing points recording
     # HIP events on the launch stream between kernels -> per-kernel durations.
-    evs = [[_event(hip) for _ in range(_lib.MOE_TIMING_POINTS)] for _ in range(steps)]
+    npts = _lib.MOE_TIMING_POINTS
+    evs = [[[_event(hip) for _ in range(npts)] for _ in layers] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        arr = (ctypes.c_void_p * _lib.MOE_TIMING_POINTS)(*[e.value for e in evs[i]])
-        _lib.check(lib.moe_set_timing_events(arr, _lib.MOE_TIMING_POINTS))
-        step()
+        for j, lw in enumerate(layers):
+            arr = (ctypes.c_void_p * npts)(*[e.value for e in evs[i][j]])
+            _lib.check(lib.moe_set_timing_events(arr, npts))
+            call(lw)
     _lib.check(lib.moe_set_timing_events(None, 0))
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    step_ms = [_elapsed_ms(hip, e[0], e[-1]) for e in evs]
-    per_kernel = {name: statistics.fmean(_elapsed_ms(hip, e[j], e[j + 1]) for e in evs)
+    calls = [e for per_step in evs for e in per_step]
+    per_kernel = {name: statistics.fmean(_elapsed_ms(hip, e[j], e[j + 1]) for e in calls)
                   for j, name in enumerate(KERNELS)}
-    for e in evs:
+    for e in calls:
         for ev in e:
             hip.hipEventDestroy(ev)
 
-    # Expert loads (outside the timed region).
-    idx, _, _ = moe.moe_route(dv["x"], dv["w_gate"], dv["bias"])
+    # Expert loads of the first layer (outside the timed regions).
+    idx, _, _ = moe.moe_route(x, layers[0]["w_gate"], layers[0]["bias"])
     off, _, _ = moe.moe_dispatch(idx, cfg.E)
     counts = np.diff(off.cpu().numpy()).tolist()
     work = work_model(cfg, counts)
     return {
-        "cfg": cfg, "inputs": dv, "y": y, "ms_per_step": plain_ms, "ms_per_step_events": statistics.fmean(step_ms),
+        "cfg": cfg, "inputs": layers[0] | {"x": x}, "layers": layers, "y": y, "ms_per_step": plain_ms,
         "ms_per_step_with_events": wall_ms, "per_kernel_ms": per_kernel, "counts": counts, "work": work,
     }
 
@@ -284,10 +301,12 @@ def cpu_baseline(res, max_tokens: int, budget_s: float = 10.0):
 def summarize(res):
     cfg, work = res["cfg"], res["work"]
     ms = res["ms_per_step"]
+    L = cfg.layers
     return {
-        "workload": cfg.name, "T": cfg.T, "tokens_per_s": round(cfg.T / (ms * 1e-3), 2), "ms_per_step": round(ms, 4),
-        "layer_tflops": round(work["layer"]["flops"] / (ms * 1e-3) / 1e12, 2),
-        "layer_gbs": round(work["layer"]["bytes"] / (ms * 1e-3) / 1e9, 1),
+        "workload": cfg.name, "T": cfg.T, "layers": L, "tokens_per_s": round(cfg.T / (ms * 1e-3), 2),
+        "ms_per_step": round(ms, 4),
+        "layer_tflops": round(L * work["layer"]["flops"] / (ms * 1e-3) / 1e12, 2),
+        "layer_gbs": round(L * work["layer"]["bytes"] / (ms * 1e-3) / 1e9, 1),
         "roofline": roofline(res),
         "per_kernel_ms": {k: round(v, 4) for k, v in res["per_kernel_ms"].items()},
         "rows_per_expert": res["counts"], "touched_experts": work["touched_experts"],
@@ -301,7 +320,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral_decode_t16")
-    ap.add_argument("--secondary", default="mixtral_prefill_t4096")
+    ap.add_argument("--secondary", default="mixtral_prefill_t4096,mixtral_skewed_t16384,mixtral_stack32_t2048",
+                    help="comma-separated workloads also measured and reported under 'secondary', or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -338,12 +358,15 @@ def main():
     res = measure(cfg, a.steps, a.warmup)
     prim = summarize(res)
     cpu = None if a.no_cpu_baseline else cpu_baseline(res, a.cpu_tokens)
-    del res["inputs"]
-    sec = None
-    if a.secondary and a.secondary != "none" and a.secondary != a.config:
+    del res
+    sec = []
+    for name in ([] if a.secondary in ("", "none") else a.secondary.split(",")):
+        if name == a.config:
+            continue
         torch.cuda.empty_cache()
-        r2 = measure(CONFIGS[a.secondary], max(5, a.steps // 2), a.warmup)
-        sec = summarize(r2)
+        c2 = CONFIGS[name]
+        r2 = measure(c2, max(3, a.steps // (4 if c2.layers > 1 else 2)), min(a.warmup, 2 if c2.layers > 1 else a.warmup))
+        sec.append(summarize(r2))
         del r2
     out = {
         "metric": METRIC, "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,

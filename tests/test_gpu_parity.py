@@ -334,3 +334,34 @@ def test_mixtral_prefill_t4096_sampled():
 
 def test_mixtral_skewed_t16384_sampled():
     _mixtral_case("mixtral_skewed_t16384", _sample_tokens)
+
+
+def test_mixtral_stack_layers_teacher_forced():
+    """Two pre-RMSNorm residual MoE sublayers at Mixtral shape (T = 2048), each
+    checked on sampled tokens against the oracle fed the GPU's exact input."""
+    cfg = CONFIGS["mixtral_stack32_t2048"]
+    dev = torch.device("cuda:0")
+    gamma = torch.ones(cfg.d, dtype=torch.float32, device=dev)
+    h = None
+    for layer in range(2):
+        say(f"stack layer {layer}: generating")
+        lw = generate_torch(cfg, dev, layer=layer)
+        if h is None:
+            h = lw["x"].clone()
+        h_in = to_host(h).copy()
+        say(f"stack layer {layer}: block forward")
+        moe.moe_block_forward(h, gamma, 1e-5, lw["w_gate"], None, lw["w1"], lw["w3"], lw["w2"])
+        torch.cuda.synchronize()
+        h_out = widen_host(to_host(h))
+        rng = np.random.default_rng(layer)
+        tokens = np.sort(rng.choice(cfg.T, size=16, replace=False))
+        w1, w3, w2 = to_host(lw["w1"]), to_host(lw["w3"]), to_host(lw["w2"])
+        ref, u, (g, idx, w) = oracle.block_forward_ref(h_in[tokens], np.ones(cfg.d, np.float32), 1e-5,
+                                                       to_host(lw["w_gate"]), None, w1, w3, w2)
+        clear, _ = clear_tokens(g)
+        y_ref = ref - widen_host(h_in[tokens])
+        tol = BF16_TOL * np.max(np.abs(y_ref)) + 2 ** -8 * np.max(np.abs(ref))
+        err = np.max(np.abs(h_out[tokens][clear] - ref[clear]))
+        say(f"stack layer {layer}: max err {err:.3e} (tol {tol:.3e}) on {int(clear.sum())} tokens")
+        assert err <= tol
+        del lw, w1, w3, w2
