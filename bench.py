@@ -244,6 +244,64 @@ def measure(cfg, steps: int, warmup: int):
     }
 
 
+def measure_decode_latency(steps: int, Ts=(1, 2, 4, 8, 16)):
+    """Per-step latency of the decode-regime layer for small T on the Mixtral
+    decode weights, launched eagerly and replayed from a HIP graph that holds
+    the whole moe_forward (router, dispatch, expert up/down, combine)."""
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_wave_amd as moe
+    from synth import CONFIGS, generate_torch
+
+    dev = torch.device("cuda:0")
+    base = CONFIGS["mixtral_decode_t16"]
+    dv = generate_torch(base, dev)
+    out = []
+    for T in Ts:
+        cfg = base.with_(name=f"mixtral_decode_t{T}", T=T)
+        x = generate_torch(cfg.with_(d_ff=64, E=2), dev)["x"]  # only x is used; seeded per T
+        shape = moe.make_shape(T, cfg.d, cfg.d_ff, cfg.E, cfg.k, x.dtype)
+        ws = torch.empty(moe.workspace_size(shape), dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        args = (x, dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
+        for _ in range(3):
+            moe.moe_forward(*args, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            moe.moe_forward(*args, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            moe.moe_forward(*args, out=y, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            moe.moe_forward(*args, out=y, workspace=ws)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+        idx, _, _ = moe.moe_route(x, dv["w_gate"], dv["bias"])
+        off, _, _ = moe.moe_dispatch(idx, cfg.E)
+        counts = np.diff(off.cpu().numpy()).tolist()
+        touched = sum(1 for c in counts if c > 0)
+        wbytes = touched * 3 * cfg.d * cfg.d_ff * 2
+        best = min(eager_ms, graph_ms)
+        out.append({"T": T, "eager_us": round(eager_ms * 1e3, 1), "graph_us": round(graph_ms * 1e3, 1),
+                    "tokens_per_s": round(T / (best * 1e-3), 1), "touched_experts": touched,
+                    "weight_GBs": round(wbytes / (best * 1e-3) / 1e9, 1)})
+        del g
+    return out
+
+
 def roofline(res):
     cfg, work, pk = res["cfg"], res["work"], res["per_kernel_ms"]
     dom = max(("expert_up", "expert_down"), key=lambda n: pk[n])
@@ -323,6 +381,7 @@ def main():
     ap.add_argument("--secondary", default="mixtral_prefill_t4096,mixtral_skewed_t16384,mixtral_stack32_t2048",
                     help="comma-separated workloads also measured and reported under 'secondary', or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-latency", action="store_true", help="skip the small-T decode latency sweep")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json for --config from rocprofv3 --pmc CSVs (no GPU needed)")
@@ -368,6 +427,11 @@ def main():
         r2 = measure(c2, max(3, a.steps // (4 if c2.layers > 1 else 2)), min(a.warmup, 2 if c2.layers > 1 else a.warmup))
         sec.append(summarize(r2))
         del r2
+    latency = None
+    if not a.no_latency:
+        torch.cuda.empty_cache()
+        print("[bench] decode latency sweep", file=sys.stderr, flush=True)
+        latency = measure_decode_latency(a.steps)
     out = {
         "metric": METRIC, "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -375,6 +439,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "k": cfg.k,
                    "parallelism": "single GPU"},
         "roofline": prim["roofline"], "cpu_baseline": cpu, "detail": prim, "secondary": sec,
+        "decode_latency": latency,
     }
     print(json.dumps(out), flush=True)
 

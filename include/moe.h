@@ -5,7 +5,7 @@
  * formula, and section "Прямой проход в формулах", MoE equation):
  *
  *     g   = x W_g                   router logits, one per expert
- *     S   = the k largest logits    (k = 2; the others count as -inf)
+ *     S   = the k largest logits    (Mixtral: k = 2; the others count as -inf)
  *     w_i = e^{g_i} / sum_{j in S} e^{g_j}          (float32)
  *     y   = sum_{i in S} w_i (SiLU(x W1_i) * (x W3_i)) W2_i
  *
@@ -35,7 +35,7 @@
  *     positive multiple of 64 (d <= 32768, d_ff <= 65536), E outside 2..64,
  *     k outside 1..E (the pages' constructor raises ValueError for this),
  *     workspace too small.
- *   MOE_ERR_UNSUPPORTED: k != 2, E not a power of two, or an (act, wt)
+ *   MOE_ERR_UNSUPPORTED: k > 8, E not a power of two, or an (act, wt)
  *     dtype pair other than (F32, F32) and (BF16, BF16).
  *   MOE_ERR_HIP: a HIP launch failed.
  * Precision.  Router logits, the top-k softmax and the combine weights are
@@ -84,14 +84,14 @@ size_t moe_workspace_size(const moe_shape* shape);
 /* Bytes of workspace moe_expert_ffn needs (h only).  Host only. */
 size_t moe_expert_ffn_workspace_size(const moe_shape* shape);
 
-/* Router: logits g = x W_g^T (+ bias), the k largest per token and their
- * softmax weights.  ("Mixtral" page, "Прямой проход в формулах", MoE
+/* Router: logits g = x W_g^T (+ bias), the k largest per token (k <= 8) and
+ * their softmax weights.  ("Mixtral" page, "Прямой проход в формулах", MoE
  * equation; "MoE изнутри" steps 1-2.)
  *   x        [T][d] in act
  *   w_gate   [E][d] fp32
  *   bias     [E] fp32 or NULL (Mixtral has none; a Linear bias otherwise)
  *   logits   [T][E] fp32 output or NULL
- *   topk_idx [T][k] int32 output: slot 0 holds the larger logit; exactly
+ *   topk_idx [T][k] int32 output: slots in descending logit order; exactly
  *            equal logits go to the lower expert index
  *   topk_w   [T][k] fp32 output, sums to 1 per token                    */
 moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
@@ -151,6 +151,22 @@ moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float*
                              float eps, const float* w_gate, const float* bias,
                              const void* w1, const void* w3, const void* w2,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* Router load-balancing loss ("Mixtral" page, section "Load-balancing
+ * loss"): L_aux = alpha * E * sum_{s<k} sum_i f_{s,i} * P_i, where f_{s,i} is
+ * the share of tokens whose s-th largest logit is expert i (ties -> lower
+ * index) and P_i the mean over tokens of the softmax over all E logits; the
+ * statistics pool all layers and every token with a nonzero mask byte.
+ *   logits     [num_layers][T][E] fp32 (the router logits of each layer,
+ *              e.g. from moe_route's logits output)
+ *   token_mask [T] uint8 or NULL (all tokens); the same mask for every layer
+ *   loss       [1] fp32 output;  stats [(k+1)*E] fp32 output or NULL:
+ *              f_{s,i} at s*E + i, then P_i at k*E + i
+ * Uses shape->T, E, k (1 <= k <= min(E, 8); any d, d_ff, dtypes).  One
+ * workgroup; the result is bitwise deterministic.  Zero valid tokens give 0. */
+moe_status moe_aux_loss(const moe_shape* shape, const float* logits, int32_t num_layers,
+                        const uint8_t* token_mask, float alpha, float* loss, float* stats,
+                        void* stream);
 
 /* Timing points.  After a successful call with MOE_TIMING_POINTS events,
  * every moe_forward / moe_block_forward on the calling thread records

@@ -25,6 +25,7 @@ from .moe_ref import (  # noqa: F401
     moe_forward_tokens,
     rmsnorm_ref,
     route_ref,
+    router_stats_ref,
     router_logits,
     silu,
     top2,

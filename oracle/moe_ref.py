@@ -255,13 +255,13 @@ def block_forward_ref(h, gamma, eps, w_gate, bias, w1, w3, w2, k: int = 2, dtype
 # ----------------------------------------------------------------------------
 # load-balancing loss  [MIX-LB]
 # ----------------------------------------------------------------------------
-def aux_loss_ref(logits_per_layer: Sequence[np.ndarray], E: int, k: int, alpha: float = 1.0,
-                 token_mask: Optional[np.ndarray] = None, dtype=np.float64) -> float:
-    """alpha * E * sum_{s=1..k} sum_i f_{s,i} P_i over all layers' real tokens ([MIX-LB]).
+def router_stats_ref(logits_per_layer: Sequence[np.ndarray], E: int, k: int,
+                     token_mask: Optional[np.ndarray] = None, dtype=np.float64):
+    """f [k, E] and P [E] of the load-balancing loss ([MIX-LB]).
 
-    f_{s,i}: share of tokens whose slot-s expert is i (top-k of the router
-    logits); P_i: mean over tokens of the router's softmax over all E experts.
-    The statistics pool every MoE layer and every unmasked token at once.
+    f_{s,i}: share of tokens whose slot-s expert (s-th largest logit, the
+    top-k order) is i; P_i: mean over tokens of the router's softmax over all
+    E experts.  The statistics pool every MoE layer and every unmasked token.
     """
     g_all: List[np.ndarray] = []
     for g in logits_per_layer:
@@ -271,12 +271,22 @@ def aux_loss_ref(logits_per_layer: Sequence[np.ndarray], E: int, k: int, alpha: 
         g_all.append(g)
     G = np.concatenate(g_all, axis=0)
     n = G.shape[0]
-    idx = top2(G, k)
     f = np.zeros((k, E), dtype=dtype)
+    P = np.zeros(E, dtype=dtype)
+    if n == 0:
+        return f, P
+    idx = top2(G, k)
     for s in range(k):
         for i in range(E):
             f[s, i] = np.count_nonzero(idx[:, s] == i) / n
     ex = np.exp(G - G.max(axis=1, keepdims=True))
     probs = ex / ex.sum(axis=1, keepdims=True)
     P = probs.mean(axis=0)
+    return f, P
+
+
+def aux_loss_ref(logits_per_layer: Sequence[np.ndarray], E: int, k: int, alpha: float = 1.0,
+                 token_mask: Optional[np.ndarray] = None, dtype=np.float64) -> float:
+    """alpha * E * sum_{s=1..k} sum_i f_{s,i} P_i over all layers' real tokens ([MIX-LB])."""
+    f, P = router_stats_ref(logits_per_layer, E, k, token_mask, dtype)
     return float(alpha * E * np.sum(f * P[None, :]))

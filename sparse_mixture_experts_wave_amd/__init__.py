@@ -7,6 +7,7 @@ from ._lib import LIB_PATH, MoEError, load  # noqa: F401
 from .moe import (  # noqa: F401
     expert_ffn_workspace_size,
     make_shape,
+    moe_aux_loss,
     moe_block_forward,
     moe_combine,
     moe_dispatch,

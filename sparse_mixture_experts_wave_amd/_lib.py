@@ -41,6 +41,7 @@ SIGNATURES = {
     "moe_forward": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_block_forward": (ctypes.c_int, [_sp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
+    "moe_aux_loss": (ctypes.c_int, [_sp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp]),
     "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -5,8 +5,8 @@
 // "Генерация": in generation only the selected experts run; "Прямой проход в
 // формулах": the expert term (SiLU(u W_gate) * u W_up) W_down.)
 //
-// Work item = (expert, 16*NG output columns).  A workgroup of KS waves takes
-// one item at a time (grid-stride over items); wave w covers the K range
+// Work item = (touched expert, 16*NG output columns).  A workgroup of KS
+// waves takes one item at a time (grid-stride over items); wave w covers the K range
 // [w K/KS, (w+1) K/KS) in 128-wide steps.  With v_mfma_f32_16x16x32_bf16,
 // lane (m = lane%16, q = lane/16) holds k-chunk q of each 32-wide step, so
 // each load instruction reads 64 contiguous bytes of 16 weight rows and the
@@ -35,15 +35,23 @@ __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
   const int Kw = K / KS;
   const int kb = wave * Kw;
   const int tiles = N / (16 * NG);
-  const int items = E * tiles;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Work items cover only the experts that received rows, so all workgroups
+  // share the touched experts' weights however few they are.
+  int touched = 0;
+  for (int e = 0; e < E; ++e) touched += offsets[e + 1] > offsets[e];
+  const int items = touched * tiles;
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int e = item / tiles;
-    const int n0 = (item - e * tiles) * (16 * NG);
+    const int j = item / tiles;  // j-th touched expert
+    int e = 0;
+    for (int seen = -1; e < E; ++e) {
+      seen += offsets[e + 1] > offsets[e];
+      if (seen == j) break;
+    }
+    const int n0 = (item - j * tiles) * (16 * NG);
     const int lo = offsets[e];
     const int n_e = offsets[e + 1] - lo;
-    if (n_e <= 0) continue;  // untouched expert: its weights are not read
 
     const uint16_t* b0row[NG];
     const uint16_t* b1row[NG];
@@ -169,6 +177,10 @@ hipError_t launch_mb(int64_t T, const uint16_t* A, const int32_t* gather, const 
   return launch_cfg<4, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
 }
 
+// Workgroups of the grid-stride loop (8 per CU on 256 CUs): enough bytes in
+// flight to saturate HBM, without a ragged last round of one-item workgroups.
+constexpr int kStreamGrid = 2048;
+
 }  // namespace
 
 bool stream_supported(int64_t T, int d, int d_ff) {
@@ -178,12 +190,12 @@ bool stream_supported(int64_t T, int d, int d_ff) {
 hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                  const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
                                  int d_ff, int E, hipStream_t stream) {
-  return launch_mb<2, 4, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, 0, stream);
+  return launch_mb<2, 4, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, kStreamGrid, stream);
 }
 
 hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2, float* y_sorted,
                                    int64_t T, int d, int d_ff, int E, hipStream_t stream) {
-  return launch_mb<2, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, 0, stream);
+  return launch_mb<2, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, kStreamGrid, stream);
 }
 
 }  // namespace moe

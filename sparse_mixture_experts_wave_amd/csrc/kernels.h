@@ -8,11 +8,12 @@
 
 namespace moe {
 
-// Router GEMM + top-2 + two-way softmax (optionally with a fused RMSNorm that
+// Router GEMM + top-k (k <= kRouterMaxK) + softmax over the kept logits (optionally with a fused RMSNorm that
 // also writes the normalised rows u in the activation dtype).
 hipError_t launch_route(const void* x, bool x_bf16, const float* w_gate, const float* bias,
                         float* logits, int32_t* topk_idx, float* topk_w, int64_t T, int d,
-                        int E, const float* gamma, float eps, void* u_out, hipStream_t stream);
+                        int E, int k, const float* gamma, float eps, void* u_out, hipStream_t stream);
+constexpr int kRouterMaxK = 8;
 
 // Stable counting sort of (token, slot) pairs by expert.
 hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E,
@@ -61,6 +62,11 @@ hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const 
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  float* y_sorted, int64_t T, int k, int d, int d_ff, int E,
                                  hipStream_t stream);
+
+// Router load-balancing loss over [layers][T][E] logits (aux_loss.hip).
+int aux_loss_max_k();
+hipError_t launch_aux_loss(const float* logits, int64_t layers, int64_t T, int E, int k, const uint8_t* mask,
+                           float alpha, float* loss, float* stats, hipStream_t stream);
 
 // Token count at or below which the bf16 expert FFN streams weights
 // (decode regime) instead of running the tiled grouped GEMM.

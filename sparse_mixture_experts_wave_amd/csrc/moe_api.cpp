@@ -53,7 +53,8 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_INVALID_ARG, "top-k = %d outside 1..E (E = %d)", s->k, s->E);
   if (s->act != MOE_F32 && s->act != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "act dtype %d unknown", s->act);
   if (s->wt != MOE_F32 && s->wt != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "wt dtype %d unknown", s->wt);
-  if (s->k != 2) return fail(MOE_ERR_UNSUPPORTED, "top-k = %d: only k = 2 is implemented", s->k);
+  if (s->k > moe::kRouterMaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "top-k = %d: at most %d is implemented", s->k, moe::kRouterMaxK);
   if ((s->E & (s->E - 1)) != 0) return fail(MOE_ERR_UNSUPPORTED, "E = %d is not a power of two", s->E);
   if (s->act != s->wt)
     return fail(MOE_ERR_UNSUPPORTED, "dtype pair (act %d, wt %d): only (f32, f32) and (bf16, bf16)", s->act, s->wt);
@@ -119,7 +120,7 @@ moe_status run_route(const moe_shape* s, const void* x, const float* w_gate, con
                      float* logits, int32_t* idx, float* w, const float* gamma, float eps,
                      void* u_out, void* stream) {
   return hip_status(moe::launch_route(x, s->act == MOE_BF16, w_gate, bias, logits, idx, w, s->T, s->d,
-                                      s->E, gamma, eps, u_out, hs(stream)),
+                                      s->E, s->k, gamma, eps, u_out, hs(stream)),
                     "router launch");
 }
 
@@ -299,6 +300,30 @@ moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float*
   MOE_TRY(need(ws, "ws"));
   return forward_impl(shape, h_inout, w_gate, bias, w1, w3, w2, h_inout, h_inout, gamma, eps, ws, ws_bytes,
                       stream);
+}
+
+moe_status moe_aux_loss(const moe_shape* shape, const float* logits, int32_t num_layers,
+                        const uint8_t* token_mask, float alpha, float* loss, float* stats, void* stream) {
+  if (shape == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (shape->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(shape->T));
+  if (shape->E < 2 || shape->E > 64) return fail(MOE_ERR_INVALID_ARG, "E = %d outside 2..64", shape->E);
+  if (shape->k < 1 || shape->k > shape->E)
+    return fail(MOE_ERR_INVALID_ARG, "top-k = %d outside 1..E (E = %d)", shape->k, shape->E);
+  if ((shape->E & (shape->E - 1)) != 0) return fail(MOE_ERR_UNSUPPORTED, "E = %d is not a power of two", shape->E);
+  if (shape->k > moe::aux_loss_max_k())
+    return fail(MOE_ERR_UNSUPPORTED, "top-k = %d above %d", shape->k, moe::aux_loss_max_k());
+  if (num_layers < 1) return fail(MOE_ERR_INVALID_ARG, "num_layers = %d < 1", num_layers);
+  if (!(alpha >= 0.f)) return fail(MOE_ERR_INVALID_ARG, "alpha = %g must be >= 0", static_cast<double>(alpha));
+  MOE_TRY(need(loss, "loss"));
+  MOE_TRY(optional(stats, "stats"));
+  if (shape->T > 0) {
+    MOE_TRY(need(logits, "logits"));
+    if (token_mask != nullptr && (reinterpret_cast<uintptr_t>(token_mask) & 15u) != 0)
+      return fail(MOE_ERR_INVALID_ARG, "token_mask is not 16-byte aligned");
+  }
+  return hip_status(moe::launch_aux_loss(logits, num_layers, shape->T, shape->E, shape->k, token_mask, alpha, loss,
+                                         stats, hs(stream)),
+                    "aux loss launch");
 }
 
 moe_status moe_set_timing_events(void* const* events, int32_t count) {

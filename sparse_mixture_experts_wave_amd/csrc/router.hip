@@ -1,5 +1,5 @@
-// Router: g = x W_g^T (+ bias) in fp32, the two largest logits per token and
-// their two-way softmax.  ("Mixtral" textbook page, "Прямой проход в
+// Router: g = x W_g^T (+ bias) in fp32, the k largest logits per token
+// (k <= 8; Mixtral uses 2) and the softmax over them.  ("Mixtral" textbook page, "Прямой проход в
 // формулах", MoE equation; "MoE изнутри", steps 1-2: Linear router, top-k,
 // softmax over the kept logits in float32.)
 //
@@ -9,8 +9,9 @@
 // loads serves all TPB tokens.  The TPB x E partial dot products are
 // transposed through LDS: lane j of each wave sums column j over its 64
 // lanes, then wave 0 adds the four quarters, so lane j ends with the logit
-// of (token j / E, expert j % E).  The top-2 is a butterfly over the E lanes
-// of each token (E is a power of two).  Small T uses one token per workgroup
+// of (token j / E, expert j % E).  The top-k is a butterfly over the E lanes
+// of each token (E is a power of two), one round per kept expert.  Small T
+// uses one token per workgroup
 // so that T workgroups share the work.
 //
 // With gamma != nullptr the kernel also applies RMSNorm: it accumulates
@@ -40,6 +41,8 @@ __device__ __forceinline__ void load_x8(const void* x, int64_t off, float v[8]) 
   }
 }
 
+constexpr int MAX_K = 8;  // largest top-k the router supports
+
 // (v, i) beats (w, j) when larger, or equal with the lower index.
 __device__ __forceinline__ bool beats(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
     const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     const float* __restrict__ gamma, float eps, void* __restrict__ u_out,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int T, int d) {
+    int T, int d, int k) {
   constexpr int P = TPB * E;                   // logits per workgroup (<= 64)
   constexpr int COLS = P + (NORM ? TPB : 0);   // + sum of squares per token
   constexpr int LD = COLS + 1;                 // padded LDS row
@@ -145,33 +148,45 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
     const bool live = lane < P && tok < T;
     if (live && logits != nullptr) logits[static_cast<int64_t>(tok) * E + e] = g;
 
-    // Top-2 over the E lanes of each token.
-    float v1 = g, v2 = -INFINITY;
-    int i1 = e, i2 = E;
+    // Top-k over the E lanes of each token: k rounds of a max butterfly
+    // (larger logit first, equal logits -> lower expert index); the winner of
+    // a round drops out of the next.  Then the softmax over the kept logits.
+    float cand = g;
+    float top_v[MAX_K];
+    int top_i[MAX_K];
 #pragma unroll
-    for (int m = E / 2; m >= 1; m >>= 1) {
-      const float ov1 = __shfl_xor(v1, m, 64);
-      const float ov2 = __shfl_xor(v2, m, 64);
-      const int oi1 = __shfl_xor(i1, m, 64);
-      const int oi2 = __shfl_xor(i2, m, 64);
-      float n1, n2;
-      int j1, j2;
-      if (beats(v1, i1, ov1, oi1)) {
-        n1 = v1; j1 = i1;
-        if (beats(v2, i2, ov1, oi1)) { n2 = v2; j2 = i2; } else { n2 = ov1; j2 = oi1; }
-      } else {
-        n1 = ov1; j1 = oi1;
-        if (beats(v1, i1, ov2, oi2)) { n2 = v1; j2 = i1; } else { n2 = ov2; j2 = oi2; }
+    for (int s = 0; s < MAX_K; ++s) {
+      if (s >= k) break;
+      float bv = cand;
+      int bi = e;
+#pragma unroll
+      for (int m = E / 2; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (beats(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
       }
-      v1 = n1; i1 = j1; v2 = n2; i2 = j2;
+      top_v[s] = bv;
+      top_i[s] = bi;
+      if (bi == e) cand = -INFINITY;
     }
     if (live && e == 0) {
-      const float q = expf(v2 - v1);
-      const float s = 1.0f + q;
-      topk_idx[2 * static_cast<int64_t>(tok)] = i1;
-      topk_idx[2 * static_cast<int64_t>(tok) + 1] = i2;
-      topk_w[2 * static_cast<int64_t>(tok)] = 1.0f / s;
-      topk_w[2 * static_cast<int64_t>(tok) + 1] = q / s;
+      float z = 0.f, p[MAX_K];
+#pragma unroll
+      for (int s = 0; s < MAX_K; ++s) {
+        if (s >= k) break;
+        p[s] = expf(top_v[s] - top_v[0]);
+        z += p[s];
+      }
+      const float inv = 1.0f / z;
+#pragma unroll
+      for (int s = 0; s < MAX_K; ++s) {
+        if (s >= k) break;
+        topk_idx[static_cast<int64_t>(tok) * k + s] = top_i[s];
+        topk_w[static_cast<int64_t>(tok) * k + s] = s == 0 ? 1.0f / z : p[s] * inv;
+      }
     }
   }
 
@@ -210,15 +225,15 @@ constexpr int64_t kRouterOneTokenMaxT = 2048;
 template <int E, bool XBF16, bool NORM>
 hipError_t launch_e(const void* x, const float* wg, const float* bias, const float* gamma,
                     float eps, void* u_out, float* logits, int32_t* idx, float* w, int64_t T,
-                    int d, hipStream_t s) {
+                    int d, int k, hipStream_t s) {
   constexpr int TPB = (64 / E) < 8 ? (64 / E) : 8;
   if (T <= kRouterOneTokenMaxT) {
     router_top2_kernel<E, 1, XBF16, NORM><<<static_cast<unsigned>(T), 256, 0, s>>>(
-        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d, k);
   } else {
     const dim3 grid(static_cast<unsigned>((T + TPB - 1) / TPB));
     router_top2_kernel<E, TPB, XBF16, NORM><<<grid, 256, 0, s>>>(
-        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d);
+        x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d, k);
   }
   return hipGetLastError();
 }
@@ -226,27 +241,28 @@ hipError_t launch_e(const void* x, const float* wg, const float* bias, const flo
 template <int E>
 hipError_t launch_dtype(const void* x, bool x_bf16, const float* wg, const float* bias,
                         const float* gamma, float eps, void* u_out, float* logits, int32_t* idx,
-                        float* w, int64_t T, int d, hipStream_t s) {
+                        float* w, int64_t T, int d, int k, hipStream_t s) {
   if (x_bf16) {
-    return gamma ? launch_e<E, true, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s)
-                 : launch_e<E, true, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s);
+    return gamma ? launch_e<E, true, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, k, s)
+                 : launch_e<E, true, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, k, s);
   }
-  return gamma ? launch_e<E, false, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s)
-               : launch_e<E, false, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, s);
+  return gamma ? launch_e<E, false, true>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, k, s)
+               : launch_e<E, false, false>(x, wg, bias, gamma, eps, u_out, logits, idx, w, T, d, k, s);
 }
 
 }  // namespace
 
 hipError_t launch_route(const void* x, bool x_bf16, const float* w_gate, const float* bias,
                         float* logits, int32_t* topk_idx, float* topk_w, int64_t T, int d,
-                        int E, const float* gamma, float eps, void* u_out, hipStream_t stream) {
+                        int E, int k, const float* gamma, float eps, void* u_out, hipStream_t stream) {
+  if (k < 1 || k > MAX_K || k > E) return hipErrorInvalidValue;
   switch (E) {
-    case 2: return launch_dtype<2>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
-    case 4: return launch_dtype<4>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
-    case 8: return launch_dtype<8>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
-    case 16: return launch_dtype<16>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
-    case 32: return launch_dtype<32>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
-    case 64: return launch_dtype<64>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, stream);
+    case 2: return launch_dtype<2>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
+    case 4: return launch_dtype<4>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
+    case 8: return launch_dtype<8>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
+    case 16: return launch_dtype<16>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
+    case 32: return launch_dtype<32>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
+    case 64: return launch_dtype<64>(x, x_bf16, w_gate, bias, gamma, eps, u_out, logits, topk_idx, topk_w, T, d, k, stream);
     default: return hipErrorInvalidValue;
   }
 }

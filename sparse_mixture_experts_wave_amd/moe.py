@@ -164,3 +164,27 @@ def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: 
                                              _p(bias), _p(w1), _p(w3), _p(w2), _p(workspace), workspace.numel(),
                                              _stream(h)))
     return h
+
+
+def moe_aux_loss(logits: torch.Tensor, k: int = 2, alpha: float = 1.0,
+                 token_mask: Optional[torch.Tensor] = None, want_stats: bool = False):
+    """Load-balancing loss over router logits [L, T, E] (or [T, E]) -> (loss [1], stats or None).
+
+    stats is [(k+1)*E]: f_{s,i} at s*E + i, then P_i at k*E + i."""
+    logits = _gpu(logits, "logits")
+    if logits.dtype != torch.float32:
+        raise ValueError("logits must be float32")
+    if logits.dim() == 2:
+        logits = logits.unsqueeze(0)
+    L, T, E = logits.shape
+    if token_mask is not None:
+        token_mask = _gpu(token_mask, "token_mask")
+        if token_mask.dtype not in (torch.uint8, torch.bool) or token_mask.numel() != T:
+            raise ValueError("token_mask must be uint8/bool [T]")
+        token_mask = token_mask.to(torch.uint8)
+    shape = make_shape(T, 64, _D_FF_UNUSED, E, k, torch.bfloat16)
+    loss = torch.empty(1, dtype=torch.float32, device=logits.device)
+    stats = torch.empty((k + 1) * E, dtype=torch.float32, device=logits.device) if want_stats else None
+    _lib.check(_lib.load().moe_aux_loss(ctypes.byref(shape), _p(logits), int(L), _p(token_mask), float(alpha),
+                                        _p(loss), _p(stats), _stream(logits)))
+    return loss, stats

@@ -53,8 +53,7 @@ def route(lib, s, x=FAKE, wg=FAKE, idx=FAKE, w=FAKE):
     (dict(E=65), _lib.MOE_ERR_INVALID_ARG),
     (dict(k=0), _lib.MOE_ERR_INVALID_ARG),
     (dict(k=9), _lib.MOE_ERR_INVALID_ARG),      # k outside 1..E: the pages' ValueError
-    (dict(k=1), _lib.MOE_ERR_UNSUPPORTED),
-    (dict(k=3), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(E=16, k=9), _lib.MOE_ERR_UNSUPPORTED),
     (dict(E=6), _lib.MOE_ERR_UNSUPPORTED),
     (dict(act=_lib.MOE_BF16, wt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
     (dict(act=7), _lib.MOE_ERR_INVALID_ARG),
@@ -121,5 +120,5 @@ def test_python_binding_maps_status_to_exceptions(lib):
     with pytest.raises(ValueError):
         _lib.check(route(lib, shape(d=100)))
     with pytest.raises(NotImplementedError):
-        _lib.check(route(lib, shape(k=3)))
+        _lib.check(route(lib, shape(E=16, k=9)))
     _lib.check(_lib.MOE_OK)

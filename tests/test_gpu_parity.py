@@ -365,3 +365,43 @@ def test_mixtral_stack_layers_teacher_forced():
         say(f"stack layer {layer}: max err {err:.3e} (tol {tol:.3e}) on {int(clear.sum())} tokens")
         assert err <= tol
         del lw, w1, w3, w2
+
+
+# ---------------------------------------------------------------------------
+# general top-k (the pages' top_k_experts parameter; Mixtral uses 2)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,d,E,k", [(300, 256, 8, 1), (300, 256, 8, 3), (129, 512, 16, 4), (64, 256, 8, 8),
+                                      (77, 256, 64, 6)])
+def test_router_general_k(T, d, E, k):
+    say(f"router general k: T={T} d={d} E={E} k={k}")
+    cfg = small("rk", T, d, 64, E=E)
+    inp = generate(cfg, tensors=("x", "w_gate"))
+    g_ref, idx_ref, w_ref = oracle.route_ref(inp["x"], inp["w_gate"], None, k=k)
+    idx, w, _ = moe.moe_route(to_dev(inp["x"]), to_dev(inp["w_gate"]), None, k=k)
+    torch.cuda.synchronize()
+    idx, w = to_host(idx), to_host(w)
+    s = np.sort(g_ref.astype(np.float64), axis=1)[:, ::-1]
+    gaps = np.diff(-s, axis=1)  # s_j - s_{j+1} >= 0
+    ok = np.all(gaps[:, :k] > 1e-4, axis=1) if k < E else np.all(gaps[:, :k - 1] > 1e-4, axis=1)
+    assert ok.mean() > 0.8
+    assert np.array_equal(idx[ok], idx_ref[ok])  # clear tokens: same experts in the same order
+    np.testing.assert_allclose(w[ok], w_ref[ok], atol=1e-6)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    assert all(len(set(r)) == k for r in idx.tolist())
+
+
+@pytest.mark.parametrize("T,d,d_ff,k", [(500, 256, 384, 1), (300, 192, 320, 3), (16, 512, 1024, 4),
+                                         (40, 512, 512, 3), (200, 256, 256, 8)])
+def test_forward_general_k(T, d, d_ff, k):
+    say(f"forward general k: T={T} d={d} d_ff={d_ff} k={k}")
+    cfg = small("fk", T, d, d_ff).with_(k=k)
+    inp = generate(cfg)
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], None, inp["w1"], inp["w3"],
+                                                        inp["w2"], k=k)
+    dv = {key: to_dev(v) for key, v in inp.items()}
+    y = to_host(moe.moe_forward(dv["x"], dv["w_gate"], None, dv["w1"], dv["w3"], dv["w2"], k=k))
+    torch.cuda.synchronize()
+    s = np.sort(g.astype(np.float64), axis=1)[:, ::-1]
+    gaps = np.diff(-s, axis=1)
+    clear = np.all(gaps[:, :k] > 1e-4, axis=1) if k < 8 else np.ones(T, bool)
+    assert max_rel_err(y, y_ref, clear) <= BF16_TOL

@@ -412,3 +412,15 @@ def test_gather_combine_equals_index_add():
     assert np.max(np.abs(y - y_ref)) <= 1e-6 * np.max(np.abs(y_ref))
     res = np.ones_like(y)
     np.testing.assert_allclose(oracle.combine_ref(rows, inv, w, res) - y, 1.0, atol=1e-5)
+
+
+def test_router_stats_are_distributions():
+    rng = np.random.default_rng(11)
+    g = [rng.standard_normal((50, 8)) for _ in range(3)]
+    mask = rng.uniform(size=50) > 0.3
+    f, P = oracle.router_stats_ref(g, 8, 2, mask)
+    np.testing.assert_allclose(f.sum(axis=1), 1.0, rtol=1e-12)   # each slot picks one expert per token
+    np.testing.assert_allclose(P.sum(), 1.0, rtol=1e-12)          # mean of distributions
+    assert np.all(f[0] + f[1] <= 1.0 + 1e-12)                     # an expert fills at most one slot per token
+    f0, P0 = oracle.router_stats_ref(g, 8, 2, np.zeros(50, bool))
+    assert not f0.any() and not P0.any()
