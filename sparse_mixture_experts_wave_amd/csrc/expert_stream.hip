@@ -190,11 +190,17 @@ bool stream_supported(int64_t T, int d, int d_ff) {
 hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                  const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
                                  int d_ff, int E, hipStream_t stream) {
+  // Few tokens touch few experts: narrower work items (16 columns) keep every
+  // workgroup busy; the K split doubles when it divides evenly.
+  if (T <= 4 && d % 1024 == 0)
+    return launch_mb<1, 8, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, kStreamGrid, stream);
   return launch_mb<2, 4, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, kStreamGrid, stream);
 }
 
 hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2, float* y_sorted,
                                    int64_t T, int d, int d_ff, int E, hipStream_t stream) {
+  if (T <= 4)
+    return launch_mb<1, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, kStreamGrid, stream);
   return launch_mb<2, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, kStreamGrid, stream);
 }
 

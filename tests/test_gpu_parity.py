@@ -166,6 +166,8 @@ def test_combine_residual_may_alias_output():
     (300, 192, 320, "bf16", "gemm"),
     (1000, 256, 384, "bf16", "gemm"),
     (5, 512, 1024, "bf16", "stream"),
+    (3, 1024, 1024, "bf16", "stream"),
+    (2, 512, 1024, "bf16", "stream"),
     (16, 512, 1536, "bf16", "stream"),
     (30, 1024, 512, "bf16", "stream"),
     (64, 512, 1024, "bf16", "stream"),
