@@ -35,8 +35,8 @@
  *     positive multiple of 64 (d <= 32768, d_ff <= 65536), E outside 2..64,
  *     k outside 1..E (the pages' constructor raises ValueError for this),
  *     workspace too small.
- *   MOE_ERR_UNSUPPORTED: k > 8, E not a power of two, or an (act, wt)
- *     dtype pair other than (F32, F32) and (BF16, BF16).
+ *   MOE_ERR_UNSUPPORTED: k > 8, E not a power of two, T * d >= 2^31, or an
+ *     (act, wt) dtype pair other than (F32, F32) and (BF16, BF16).
  *   MOE_ERR_HIP: a HIP launch failed.
  * Precision.  Router logits, the top-k softmax and the combine weights are
  *   fp32 (the pages compute the router softmax in float32).  Expert GEMMs

@@ -6,38 +6,76 @@
 // term; w1 = gate, w3 = up, w2 = down per the page's HuggingFace mapping.)
 //
 // Tiling.  One 512-thread workgroup computes a 256-row x 256-column tile of
-// (rows of one expert) x (weight rows), K staged through LDS in 64-wide
-// double-buffered slices (2 x 64 KiB).  For the up projection the 256 weight
-// rows are 128 rows of W1 and the same 128 rows of W3, so the SiLU(gate) * up
-// product is formed in registers and only h is written.  The eight waves sit
-// 2 (rows) x 4 (columns); each computes 128 x 64 with v_mfma_f32_32x32x16_bf16
-// (4 x 2 blocks of 32x32, 128 fp32 accumulators per lane), two waves per SIMD.
+// (rows of one expert) x (weight rows).  For the up projection the 256 weight
+// rows are 128 rows of W1 and the same 128 rows of W3, so SiLU(gate) * up is
+// formed in registers and only h is written.  The eight waves sit 2 (rows) x 4
+// (columns); each computes 128 x 64 with v_mfma_f32_32x32x16_bf16 (4 x 2
+// blocks of 32x32, 128 fp32 accumulators per lane).
 //
-// LDS layout: row r of a [256][64] bf16 tile holds its eight 16-byte chunks
-// at chunk position c ^ ((r >> 1) & 7), so the 16 consecutive rows an MFMA
-// operand fetch touches fall in distinct 16-byte bank groups of the 64-bank
-// LDS, and the 1 KiB a wave writes per store instruction is contiguous.
+// Ping-pong schedule.  Waves 0-3 (group 0) and 4-7 (group 1) put one wave of
+// each group on every SIMD, and the groups run half a step apart: while one
+// group issues the 16 MFMAs of a 32-wide K slice, the other reads its next
+// slice's operands from LDS and issues its share of the global -> LDS copies.
+// Every such interval ends in a barrier of all eight waves, so the matrix core
+// of each SIMD always has one wave feeding it.  Group 0 copies the A slices,
+// group 1 the B slices.
+//
+// Data movement.  K is staged in 32-wide slices through a ring of NS = 4 LDS
+// slots (4 x 32 KiB).  Copies go straight from memory to LDS
+// (buffer_load_dwordx4 ... lds: no staging registers, no LDS store
+// instructions) through one buffer descriptor per wave.  The copy of slice s+3
+// is issued in the memory phase of slice s, into the slot of slice s-1 (whose
+// last reader finished one interval before), and each wave waits for its own
+// copies of slice s+1 (s_waitcnt vmcnt) just before the barrier that opens it.
+//
+// LDS layout: a slice is [256 rows][32] bf16, 64 bytes per row; row r keeps
+// its four 16-byte chunks at position c ^ ((r >> 2) & 3), so the 16
+// consecutive rows that one operand read touches land in 16 distinct 16-byte
+// bank groups of the 64-bank LDS.  A copy instruction writes 1 KiB (16 rows)
+// contiguously; each lane picks the global chunk that belongs at its slot.
 //
 // Ragged expert tails.  Row tiles are numbered per expert (ceil(n_e / 256)
 // each); a tile's 32-row slices past the expert's last row skip their MFMAs.
+// Rows past the last one (and weight rows past N) are clamped to valid rows:
+// their products land in rows / columns the epilogue never stores.
 //
 // Tile order.  Consecutive tile numbers walk one expert in groups of 8 column
 // tiles x all of its row tiles, so blocks that share a weight tile (or an
-// activation tile) are numbered, hence dispatched, together.
+// activation tile) are numbered together.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 256;       // rows (tokens) per tile
-constexpr int BNR = 256;      // weight rows per tile
-constexpr int BK = 64;        // K per LDS stage
-constexpr int NTHR = 512;     // 8 waves
-constexpr int NGROUP = 8;     // column tiles per tile-order group
-constexpr int TILE_ELEMS = BM * BK;
+constexpr int BM = 256;    // rows (tokens) per tile
+constexpr int BNR = 256;   // weight rows per tile
+constexpr int BK = 32;     // K per LDS slice
+constexpr int NS = 4;      // LDS ring depth (slices)
+constexpr int NTHR = 512;  // 8 waves
+constexpr int NGROUP = 8;  // column tiles per tile-order group
+constexpr int SLICE = BM * BK;  // elements per operand slice
+constexpr int COPIES = 4;       // copy instructions per thread per slice
 
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 3); }
+static_assert(2 * NS * SLICE * 2 <= 163840, "LDS ring exceeds 160 KiB");
+
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ ((r >> 2) & 3)) << 3); }
+
+// s_waitcnt with only a vmcnt limit (expcnt, lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt left unconstrained).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// A barrier that the compiler may not move any instruction across.
+__device__ __forceinline__ void bar() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct Tile {
   int e, m0, rows, n0;
@@ -70,7 +108,7 @@ __device__ __forceinline__ bool map_tile(const int32_t* __restrict__ offsets, in
   return false;
 }
 
-// Fragments of one 16-wide k-step: four 32-row A slices and two 32-row B slices.
+// Operands of one 16-wide k-step: four 32-row A slices and two 32-row B slices.
 struct Frag {
   bf16x8 a[4], b[2];
 };
@@ -92,7 +130,7 @@ __device__ __forceinline__ void read_frag(const uint16_t* As, const uint16_t* Bs
 }
 
 // FULL: every 32-row slice of the tile holds rows; otherwise slices past
-// the last row (wave-uniform test) skip their MFMAs.
+// the last row (a wave-uniform test) skip their MFMAs.
 template <bool FULL>
 __device__ __forceinline__ void mma(const Frag& f, const bool (&live)[4], f32x16 (&acc)[4][2]) {
 #pragma unroll
@@ -102,67 +140,133 @@ __device__ __forceinline__ void mma(const Frag& f, const bool (&live)[4], f32x16
       if (FULL || live[mi]) acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[nb], acc[mi][nb], 0, 0, 0);
 }
 
-// Software pipeline, per 64-wide K stage kt (LDS buffer kt % 2):
-//   k-step 0: store stage kt+1 (loaded one stage earlier) into the other LDS
-//             buffer, issue the global loads of stage kt+2, read fragments of
-//             k-step 1, MFMAs of k-step 0;
-//   k-steps 1, 2: read the next k-step's fragments, MFMAs;
-//   k-step 3: barrier (stage kt+1 complete in LDS, stage kt fully read), read
-//             k-step 0 of stage kt+1, MFMAs of k-step 3.
-template <bool GATED, bool FULL>
-__device__ __forceinline__ void mainloop(const uint16_t* const (&a_src)[4], const uint16_t* const (&b_src)[4],
-                                         const int (&lds_off)[4], uint16_t* sA, uint16_t* sB, int K,
-                                         int rows, f32x16 (&acc)[4][2]) {
+// The LDS ring: NS slices of A and of B, each a distinct array, so that the
+// compiler can tell a copy into one slot from an operand read of another
+// (slot indices below are compile-time constants).
+__shared__ __attribute__((aligned(1024))) uint16_t lds_a0[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_a1[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_a2[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_a3[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_b0[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_b1[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_b2[SLICE];
+__shared__ __attribute__((aligned(1024))) uint16_t lds_b3[SLICE];
+
+template <int B>
+__device__ __forceinline__ uint16_t* ring_a() {
+  static_assert(B >= 0 && B < NS, "slot");
+  if constexpr (B == 0) return lds_a0;
+  else if constexpr (B == 1) return lds_a1;
+  else if constexpr (B == 2) return lds_a2;
+  else return lds_a3;
+}
+template <int B>
+__device__ __forceinline__ uint16_t* ring_b() {
+  static_assert(B >= 0 && B < NS, "slot");
+  if constexpr (B == 0) return lds_b0;
+  else if constexpr (B == 1) return lds_b1;
+  else if constexpr (B == 2) return lds_b2;
+  else return lds_b3;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Where this thread's copies come from: the wave's buffer descriptor and the
+// byte offset of each of its four 16-byte chunks at K = 0.
+struct CopySrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[COPIES];
+};
+
+// Copy K slice `s` of this wave group's operand into ring slot B: group 0
+// (waves 0-3) copies A, group 1 (waves 4-7) copies B.  Wave w's copy j fills
+// rows 64 (w & 3) + 16 j + lane / 4, slot lane % 4 of each row.
+template <int B>
+__device__ __forceinline__ void copy_slice(const CopySrc& cs, int s) {
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 2;
+  const uint32_t k0 = s * (BK * 2);
+  uint16_t* ring = (wave >> 2) == 0 ? ring_a<B>() : ring_b<B>();
+#pragma unroll
+  for (int j = 0; j < COPIES; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs.rsrc, (lds_ptr)(ring + ((wave & 3) * 64 + j * 16) * BK), 16,
+                                             cs.off[j] + k0, 0, 0, 0);
+}
+
+// Wait until this wave's copies of slice s+1 have landed, leaving those of
+// the later slices already issued (up to s+3) in flight.
+__device__ __forceinline__ void wait_slice_next(int s, int KT) {
+  if (s + 3 < KT) wait_vmcnt<2 * COPIES>();
+  else if (s + 2 < KT) wait_vmcnt<COPIES>();
+  else wait_vmcnt<0>();
+}
+
+// One K slice s (ring slot B = s % NS), as two intervals: memory phase
+// (operand reads of slice s, copies of slice s+3) and compute phase (16
+// MFMAs).  Group 1 runs each phase one interval after group 0, so every
+// interval pairs one group's memory phase with the other's compute phase.
+// The wait for slice s+1 sits at the end of the interval both groups share
+// before slice s+1 is first read (group 0's compute phase, group 1's memory
+// phase of slice s).
+template <bool GATED, bool FULL, int B>
+__device__ __forceinline__ void slice_step(const CopySrc& cs, int s, int KT, int grp, const bool (&live)[4],
+                                           f32x16 (&acc)[4][2]) {
+  constexpr int FILL = (B + NS - 1) % NS;
+  Frag f0, f1;
+  read_frag<GATED>(ring_a<B>(), ring_b<B>(), 0, f0);
+  read_frag<GATED>(ring_a<B>(), ring_b<B>(), 1, f1);
+  if (s + NS - 1 < KT) copy_slice<FILL>(cs, s + NS - 1);
+  wait_lgkm0();
+  if (grp == 1) wait_slice_next(s, KT);
+  bar();
+  mma<FULL>(f0, live, acc);
+  mma<FULL>(f1, live, acc);
+  if (grp == 0) wait_slice_next(s, KT);
+  bar();
+}
+
+template <bool GATED, bool FULL>
+__device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
+  const int wave = threadIdx.x >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   bool live[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) live[mi] = FULL || (wm * 128 + mi * 32 < rows);
+  for (int mi = 0; mi < 4; ++mi) live[mi] = FULL || (grp * 128 + mi * 32 < rows);
 
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = load16(a_src[i] + k0);
-      rb[i] = load16(b_src[i] + k0);
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      store16(sA + buf * TILE_ELEMS + lds_off[i], ra[i]);
-      store16(sB + buf * TILE_ELEMS + lds_off[i], rb[i]);
-    }
-  };
-
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  if (KT > 1) gload(1);
-  __syncthreads();
-  Frag f0, f1;
-  read_frag<GATED>(sA, sB, 0, f0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    const uint16_t* As = sA + cur * TILE_ELEMS;
-    const uint16_t* Bs = sB + cur * TILE_ELEMS;
-    // k-step 0
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    if (kt + 2 < KT) gload(kt + 2);
-    read_frag<GATED>(As, Bs, 1, f1);
-    mma<FULL>(f0, live, acc);
-    // k-step 1
-    read_frag<GATED>(As, Bs, 2, f0);
-    mma<FULL>(f1, live, acc);
-    // k-step 2
-    read_frag<GATED>(As, Bs, 3, f1);
-    mma<FULL>(f0, live, acc);
-    // k-step 3
-    __syncthreads();
-    if (kt + 1 < KT) read_frag<GATED>(sA + (cur ^ 1) * TILE_ELEMS, sB + (cur ^ 1) * TILE_ELEMS, 0, f0);
-    mma<FULL>(f1, live, acc);
+  const int KT = K / BK;  // >= 2 (K is a multiple of 64)
+  // Prologue: slices 0 .. NS-2 in flight; wait for slice 0.
+  copy_slice<0>(cs, 0);
+  copy_slice<1>(cs, 1);
+  if (2 < KT) copy_slice<2>(cs, 2);
+  if (KT >= 3)
+    wait_vmcnt<2 * COPIES>();
+  else
+    wait_vmcnt<COPIES>();
+  bar();
+  if (grp == 1) bar();  // group 1 starts one interval late
+  int s = 0;
+  for (; s + NS <= KT; s += NS) {
+    slice_step<GATED, FULL, 0>(cs, s, KT, grp, live, acc);
+    slice_step<GATED, FULL, 1>(cs, s + 1, KT, grp, live, acc);
+    slice_step<GATED, FULL, 2>(cs, s + 2, KT, grp, live, acc);
+    slice_step<GATED, FULL, 3>(cs, s + 3, KT, grp, live, acc);
   }
+  if (s < KT) slice_step<GATED, FULL, 0>(cs, s, KT, grp, live, acc);
+  if (s + 1 < KT) slice_step<GATED, FULL, 1>(cs, s + 1, KT, grp, live, acc);
+  if (s + 2 < KT) slice_step<GATED, FULL, 2>(cs, s + 2, KT, grp, live, acc);
+  if (grp == 0) bar();  // ... and group 0 ends one interval late: same barrier count
+}
+
+// A buffer descriptor over [base, base + 4 GiB).  base is the same in every
+// lane of the wave; reading it through readfirstlane keeps the descriptor in
+// scalar registers.  (Both halves are widened as unsigned: a sign-extended low
+// half would corrupt the high half of the address.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* base) {
+  const uint64_t bits = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits >> 32)));
+  // Raw buffer: stride 0, num_records = 4 GiB - 1 bytes, 32-bit data format word.
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), (short)0,
+                                           static_cast<int>(0xFFFFFFFFu), 0x00020000);
 }
 
 template <bool GATED>
@@ -170,46 +274,43 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, void* __restrict__ out, int N, int K, int NT) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2 * TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2 * TILE_ELEMS];
-
-  const int L = blockIdx.x;
   constexpr int COLS = GATED ? BNR / 2 : BNR;  // output columns per tile
   Tile t;
-  if (!map_tile(offsets, E, NT, COLS, L, t)) return;
+  if (!map_tile(offsets, E, NT, COLS, blockIdx.x, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 2;
   const int wn = wave & 3;
-  const int chunk = tid & 7;
 
-  // Global->LDS copy assignment: thread copies chunk `chunk` of tile rows
-  // tid/8 + 64 i of both operands.
-  // Rows past the expert's last row and weight rows past N are clamped to
-  // valid ones: the products they feed land in rows / columns that the
-  // epilogue never stores, so the loads need no predication.
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[4];
-  int lds_off[4];
+  // Copy sources.  Group 0: the activation rows (gathered through
+  // sorted_token for the up projection; for the down projection the tile's
+  // rows of h are contiguous, so the descriptor starts at the tile).  Group 1:
+  // the tile's weight rows of W1 (waves 4, 5) or W3 (waves 6, 7) in the up
+  // projection, of W2 in the down projection.  Every offset stays below 4 GiB:
+  // the host requires T*d and d*d_ff below 2^31 elements.
+  CopySrc cs;
+  const uint16_t* base;
+  if (wave < 4) {
+    base = gather ? A : A + static_cast<int64_t>(t.m0) * K;
+  } else {
+    const uint16_t* Bm = (GATED && (wave & 3) >= 2) ? B1 : B0;
+    base = Bm + (static_cast<int64_t>(t.e) * N + t.n0) * K;
+  }
+  cs.rsrc = wave_rsrc(base);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 64 * i;
-    const int rr = t.m0 + min(r, t.rows - 1);
-    const int src = gather ? gather[rr] : rr;
-    a_src[i] = A + static_cast<int64_t>(src) * K + chunk * 8;
-    int n;
-    const uint16_t* Bm;
-    if (GATED) {
-      Bm = r < 128 ? B0 : B1;
-      n = t.n0 + (r & 127);
+  for (int j = 0; j < COPIES; ++j) {
+    const int r = (wave & 3) * 64 + j * 16 + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((r >> 2) & 3);
+    int row;
+    if (wave < 4) {
+      const int rr = min(r, t.rows - 1);
+      row = gather ? gather[t.m0 + rr] : rr;
     } else {
-      Bm = B0;
-      n = t.n0 + r;
+      row = min(GATED ? (r & 127) : r, N - 1 - t.n0);
     }
-    b_src[i] = Bm + (static_cast<int64_t>(t.e) * N + min(n, N - 1)) * K + chunk * 8;
-    lds_off[i] = swz(r, chunk);
+    cs.off[j] = (static_cast<uint32_t>(row) * K + chunk * 8) * 2;
   }
 
   f32x16 acc[4][2];
@@ -221,9 +322,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
       for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
 
   if (t.rows == BM)
-    mainloop<GATED, true>(a_src, b_src, lds_off, sA, sB, K, t.rows, acc);
+    mainloop<GATED, true>(cs, K, t.rows, acc);
   else
-    mainloop<GATED, false>(a_src, b_src, lds_off, sA, sB, K, t.rows, acc);
+    mainloop<GATED, false>(cs, K, t.rows, acc);
 
   // Epilogue.  32x32 accumulator layout: lane holds column lane%32 and rows
   // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.

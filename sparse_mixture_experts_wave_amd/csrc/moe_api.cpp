@@ -61,6 +61,10 @@ moe_status check_shape(const moe_shape* s) {
   // Row indices are int32 on the device.
   if (s->T > (int64_t{1} << 30) / s->k)
     return fail(MOE_ERR_INVALID_ARG, "T = %lld too large", static_cast<long long>(s->T));
+  // The prefill GEMM addresses gathered activation rows with 32-bit byte offsets.
+  if (s->T * s->d >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * d = %lld: at most 2^31 - 1 activation elements per call",
+                static_cast<long long>(s->T * s->d));
   return MOE_OK;
 }
 

@@ -57,6 +57,7 @@ def route(lib, s, x=FAKE, wg=FAKE, idx=FAKE, w=FAKE):
     (dict(E=6), _lib.MOE_ERR_UNSUPPORTED),
     (dict(act=_lib.MOE_BF16, wt=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
     (dict(act=7), _lib.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 25, d=64), _lib.MOE_ERR_UNSUPPORTED),  # T * d = 2^31: 32-bit activation offsets
 ])
 def test_shape_validation(lib, kw, status):
     assert route(lib, shape(**kw)) == status
