@@ -23,6 +23,11 @@ Sources (all on the pages this project follows):
   [MIX-LB] same page, section "Load-balancing loss".
   [MIX-HF] same page, section "Загрузка весов HuggingFace": router w1/w3/w2
            map to gate/up/down.
+  [MIX-B]  same page, section "Конфигурация" (the `bias` key: a bias on every
+           Linear, the experts' included, on by default, off in Mixtral 8x7B)
+           and the teaching-config table of "Подсчёт параметров" (each Linear
+           gains d_out bias parameters): an expert with biases is
+           (SiLU(u W_gate + b_gate) * (u W_up + b_up)) W_down + b_down.
 
 Precision: fp32 by default, as the pages fix the router softmax in float32 and
 the layer's oracle is stated in fp32; every function also runs in fp64 (pass
@@ -105,23 +110,41 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1 + np.exp(-z))
 
 
-def expert_swiglu(u, w1_e, w3_e, w2_e, dtype=np.float32) -> np.ndarray:
+def expert_swiglu(u, w1_e, w3_e, w2_e, dtype=np.float32, b1_e=None, b3_e=None, b2_e=None) -> np.ndarray:
     """(SiLU(u W_gate) * (u W_up)) W_down for rows u ([MIX-F]); w1 = gate, w3 = up, w2 = down ([MIX-HF]).
 
-    w1_e, w3_e are [d_ff, d] and w2_e is [d, d_ff] (nn.Linear layout).
+    w1_e, w3_e are [d_ff, d] and w2_e is [d, d_ff] (nn.Linear layout).  The
+    optional Linear biases b1_e, b3_e [d_ff] and b2_e [d] enter each
+    projection's output ([MIX-B]); None means that Linear has no bias.
     """
     u = widen(u, dtype)
     a = u @ widen(w1_e, dtype).T
+    if b1_e is not None:
+        a = a + widen(b1_e, dtype)
     b = u @ widen(w3_e, dtype).T
+    if b3_e is not None:
+        b = b + widen(b3_e, dtype)
     h = silu(a) * b
-    return (h @ widen(w2_e, dtype).T).astype(dtype, copy=False)
+    y = h @ widen(w2_e, dtype).T
+    if b2_e is not None:
+        y = y + widen(b2_e, dtype)
+    return y.astype(dtype, copy=False)
+
+
+def _expert_bias(eb, e):
+    """(b1[e], b3[e], b2[e]) from eb = (b1 [E, d_ff] | None, b3 [E, d_ff] | None, b2 [E, d] | None)."""
+    if eb is None:
+        return None, None, None
+    return tuple(None if b is None else b[e] for b in eb)
 
 
 # ----------------------------------------------------------------------------
 # O1: the definition, one token at a time  [MIX-F], [MIX-A] ("naive token loop")
 # ----------------------------------------------------------------------------
-def moe_forward_token_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32):
-    """y_t = sum_{i in S_t} w_i SwiGLU_i(x_t), token by token.  Small inputs only."""
+def moe_forward_token_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32, eb=None):
+    """y_t = sum_{i in S_t} w_i SwiGLU_i(x_t), token by token.  Small inputs only.
+
+    eb: optional expert biases (b1, b3, b2), see expert_swiglu."""
     g, idx, w = route_ref(x, w_gate, bias, k, dtype)
     X = widen(x, dtype)
     T, d = X.shape
@@ -138,7 +161,7 @@ def moe_forward_token_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.flo
         for s in range(k):
             e = int(idx[t, s])
             a, b, c = weights(e)
-            acc = acc + w[t, s] * expert_swiglu(X[t:t + 1], a, b, c, dtype)[0]
+            acc = acc + w[t, s] * expert_swiglu(X[t:t + 1], a, b, c, dtype, *_expert_bias(eb, e))[0]
         y[t] = acc
     return y, (g, idx, w)
 
@@ -146,7 +169,7 @@ def moe_forward_token_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.flo
 # ----------------------------------------------------------------------------
 # O2: the pages' expert-major algorithm  [MIX-A]
 # ----------------------------------------------------------------------------
-def moe_forward_expert_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32):
+def moe_forward_expert_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32, eb=None):
     """Loop over experts: gather the expert's tokens (row-major where), skip empty
     experts, index-add the weighted expert output into Y ([MIX-A])."""
     g, idx, w = route_ref(x, w_gate, bias, k, dtype)
@@ -158,19 +181,19 @@ def moe_forward_expert_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.fl
         tok, slot = np.nonzero(idx == e)
         if tok.size == 0:
             continue
-        out = expert_swiglu(X[tok], w1[e], w3[e], w2[e], dtype)
+        out = expert_swiglu(X[tok], w1[e], w3[e], w2[e], dtype, *_expert_bias(eb, e))
         np.add.at(Y, tok, w[tok, slot][:, None] * out)
     return Y, (g, idx, w)
 
 
-def moe_forward_tokens(x_rows, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32):
+def moe_forward_tokens(x_rows, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32, eb=None):
     """The layer on a subset of token rows.
 
     The MoE acts on each position independently (same page, exercise 6 of
     "Вопросы и упражнения"), so a sample of rows can be checked on its own.
     Uses the expert-major form; returns (y_rows, (g, idx, w)).
     """
-    return moe_forward_expert_loop(x_rows, w_gate, bias, w1, w3, w2, k, dtype)
+    return moe_forward_expert_loop(x_rows, w_gate, bias, w1, w3, w2, k, dtype, eb)
 
 
 # ----------------------------------------------------------------------------
@@ -215,7 +238,7 @@ def combine_ref(y_sorted, inv_pos, topk_w, residual=None, dtype=np.float32) -> n
     return out
 
 
-def expert_rows_ref(x, sorted_token, offsets, w1, w3, w2, dtype=np.float32) -> np.ndarray:
+def expert_rows_ref(x, sorted_token, offsets, w1, w3, w2, dtype=np.float32, eb=None) -> np.ndarray:
     """y_sorted[r] = Expert_e(x[sorted_token[r]]) for the rows of every expert e ([MIX-A], [MIX-F])."""
     E = len(offsets) - 1
     X = widen(x, dtype)
@@ -224,7 +247,7 @@ def expert_rows_ref(x, sorted_token, offsets, w1, w3, w2, dtype=np.float32) -> n
     for e in range(E):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
-            out[lo:hi] = expert_swiglu(X[sorted_token[lo:hi]], w1[e], w3[e], w2[e], dtype)
+            out[lo:hi] = expert_swiglu(X[sorted_token[lo:hi]], w1[e], w3[e], w2[e], dtype, *_expert_bias(eb, e))
     return out
 
 
@@ -241,14 +264,14 @@ def rmsnorm_ref(z, gamma=None, eps: float = 1e-5, dtype=np.float32) -> np.ndarra
     return out.astype(dtype, copy=False)
 
 
-def block_forward_ref(h, gamma, eps, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32):
+def block_forward_ref(h, gamma, eps, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32, eb=None):
     """H = U + MoE(RMSNorm_2(U)) ([MIX-F], pre-LN block, MoE half).
 
     Returns (h_out, u, (g, idx, w)) with u the normalised input of the MoE.
     """
     U = widen(h, dtype)
     u = rmsnorm_ref(U, gamma, eps, dtype)
-    y, route = moe_forward_expert_loop(u, w_gate, bias, w1, w3, w2, k, dtype)
+    y, route = moe_forward_expert_loop(u, w_gate, bias, w1, w3, w2, k, dtype, eb)
     return (U + y).astype(dtype, copy=False), u, route
 
 

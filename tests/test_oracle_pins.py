@@ -346,17 +346,128 @@ def test_aux_loss_collapsed_router_equals_alpha_E():
 
 
 # ---------------------------------------------------------------------------
+# expert Linear biases ("Конфигурация", `bias` key; "Подсчёт параметров")
+# ---------------------------------------------------------------------------
+def _torch_swiglu_linear(u, w1, w3, w2, b1, b3, b2):
+    """The biased expert through torch's own Linear (F.linear adds the bias)."""
+    F = torch.nn.functional
+    return F.linear(F.silu(F.linear(u, w1, b1)) * F.linear(u, w3, b3), w2, b2)
+
+
+def _tiny_bias(seed, E=8, d=16, d_ff=24):
+    rng = np.random.default_rng(100 + seed)
+    return (rng.standard_normal((E, d_ff)).astype(np.float32) * 0.5,
+            rng.standard_normal((E, d_ff)).astype(np.float32) * 0.5,
+            rng.standard_normal((E, d)).astype(np.float32) * 0.5)
+
+
+def _pair_bruteforce_torch_bias(x, wg, b, w1, w3, w2, eb):
+    """As _pair_bruteforce_torch, each expert evaluated by torch's biased Linear."""
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    X, WG = t(x), t(wg)
+    G = X @ WG.T + (t(b) if b is not None else 0)
+    T = G.shape[0]
+    y = torch.zeros_like(X)
+    ok = np.ones(T, bool)
+    for tt in range(T):
+        gt = G[tt]
+        srt = torch.sort(gt, descending=True).values
+        ok[tt] = bool(srt[1] - srt[2] > 1e-3)
+        i, j = _pair_argmax(gt.tolist())
+        wts = torch.softmax(torch.stack([gt[i], gt[j]]), dim=0)
+        for wgt, e in zip(wts, (i, j)):
+            y[tt] += wgt * _torch_swiglu_linear(X[tt:tt + 1], t(w1[e]), t(w3[e]), t(w2[e]),
+                                                t(eb[0][e]), t(eb[1][e]), t(eb[2][e]))[0]
+    return y.numpy(), ok
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_biased_experts_equal_28_pair_bruteforce(seed):
+    x, wg, w1, w3, w2 = _tiny(seed)
+    eb = _tiny_bias(seed)
+    y1, _ = oracle.moe_forward_token_loop(x, wg, None, w1, w3, w2, eb=eb)
+    y2, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, w2, eb=eb)
+    ref, ok = _pair_bruteforce_torch_bias(x, wg, None, w1, w3, w2, eb)
+    assert ok.sum() >= len(ok) // 2
+    for y in (y1, y2):
+        assert np.max(np.abs(y[ok] - ref[ok])) <= 1e-5 * np.max(np.abs(ref[ok]))
+
+
+def test_biased_identity_when_all_experts_equal():
+    x, wg, w1, w3, w2 = _tiny(2)
+    b1, b3, b2 = _tiny_bias(2)
+    rep = lambda a: np.broadcast_to(a[5], a.shape).copy()
+    W1, W3, W2, B1, B3, B2 = map(rep, (w1, w3, w2, b1, b3, b2))
+    y, _ = oracle.moe_forward_expert_loop(x, wg, None, W1, W3, W2, eb=(B1, B3, B2))
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    dense = _torch_swiglu_linear(t(x), t(W1[0]), t(W3[0]), t(W2[0]), t(B1[0]), t(B3[0]), t(B2[0])).numpy()
+    assert np.max(np.abs(y - dense)) <= 1e-5 * np.max(np.abs(dense))
+
+
+def test_biases_closed_forms():
+    """Zero weights leave only the biases: with W2 = 0 the layer is sum_s w_s b2[e_s];
+    with W1 = W3 = 0 every row of expert e is SiLU(b1[e]) * b3[e] through W2, plus b2[e]."""
+    x, wg, w1, w3, w2 = _tiny(3)
+    b1, b3, b2 = _tiny_bias(3)
+    _, idx, w = oracle.route_ref(x, wg, None)
+    y, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, np.zeros_like(w2), eb=(b1, b3, b2))
+    ref = sum(w[:, s:s + 1].astype(np.float64) * b2[idx[:, s]] for s in range(2))
+    assert np.max(np.abs(y - ref)) <= 1e-6
+    y, _ = oracle.moe_forward_expert_loop(x, wg, None, np.zeros_like(w1), np.zeros_like(w3), w2, eb=(b1, b3, b2))
+    h = scipy.special.expit(b1.astype(np.float64)) * b1 * b3  # [E, d_ff]
+    per_e = np.einsum("ef,edf->ed", h, w2.astype(np.float64)) + b2
+    ref = sum(w[:, s:s + 1].astype(np.float64) * per_e[idx[:, s]] for s in range(2))
+    assert np.max(np.abs(y - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+def test_zero_biases_equal_no_biases():
+    x, wg, w1, w3, w2 = _tiny(4)
+    z = (np.zeros((8, 24), np.float32), np.zeros((8, 24), np.float32), np.zeros((8, 16), np.float32))
+    y0, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, w2)
+    y1, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, w2, eb=z)
+    assert np.array_equal(y0, y1)
+    # each bias may be absent on its own
+    y2, _ = oracle.moe_forward_expert_loop(x, wg, None, w1, w3, w2, eb=(None, z[1], None))
+    assert np.array_equal(y0, y2)
+
+
+def _mut_bias_after_silu(u, w1_e, w3_e, w2_e, dtype=np.float32, b1_e=None, b3_e=None, b2_e=None):
+    u = moe_ref.widen(u, dtype)
+    a = moe_ref.silu(u @ moe_ref.widen(w1_e, dtype).T) + b1_e
+    h = a * (u @ moe_ref.widen(w3_e, dtype).T + b3_e)
+    return (h @ moe_ref.widen(w2_e, dtype).T + b2_e).astype(dtype)
+
+
+def _mut_down_bias_dropped(u, w1_e, w3_e, w2_e, dtype=np.float32, b1_e=None, b3_e=None, b2_e=None):
+    return _orig_expert(u, w1_e, w3_e, w2_e, dtype, b1_e, b3_e, None)
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("gate bias after SiLU", _mut_bias_after_silu),
+    ("down bias dropped", _mut_down_bias_dropped),
+])
+def test_planted_bias_mistake_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(moe_ref, "expert_swiglu", mutant)
+    x, wg, w1, w3, w2 = _tiny(0)
+    eb = _tiny_bias(0)
+    y, _ = moe_ref.moe_forward_token_loop(x, wg, None, w1, w3, w2, eb=eb)
+    monkeypatch.undo()
+    ref, ok = _pair_bruteforce_torch_bias(x, wg, None, w1, w3, w2, eb)
+    assert np.max(np.abs(y[ok] - ref[ok])) > 1e-3 * np.max(np.abs(ref[ok])), name
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: a mutated copy of the oracle must fail a pin
 # ---------------------------------------------------------------------------
 def _mut_silu_sign(z):
     return z / (1 + np.exp(z))
 
 
-def _mut_swap_gate_up(u, w1_e, w3_e, w2_e, dtype=np.float32):
+def _mut_swap_gate_up(u, w1_e, w3_e, w2_e, dtype=np.float32, *biases):
     return _orig_expert(u, w3_e, w1_e, w2_e, dtype)
 
 
-def _mut_transpose_down(u, w1_e, w3_e, w2_e, dtype=np.float32):
+def _mut_transpose_down(u, w1_e, w3_e, w2_e, dtype=np.float32, *biases):
     u = moe_ref.widen(u, dtype)
     h = moe_ref.silu(u @ moe_ref.widen(w1_e, dtype).T) * (u @ moe_ref.widen(w3_e, dtype).T)
     w2 = moe_ref.widen(w2_e, dtype)
