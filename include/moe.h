@@ -75,6 +75,21 @@ typedef struct {
   int32_t wt;  /* moe_dtype */
 } moe_shape;
 
+/* Optional per-expert Linear biases ("Mixtral" page, section "Конфигурация":
+ * the `bias` key puts a bias on every Linear, the experts' included; it is on
+ * by default there and off in Mixtral 8x7B).  With them an expert computes
+ *   (SiLU(u W1_e^T + b1_e) * (u W3_e^T + b3_e)) W2_e^T + b2_e.
+ * Each pointer may be NULL (that projection has no bias), and so may the
+ * struct itself.  Device memory in the weight dtype wt, 16-byte aligned,
+ * owned by the caller, read only:
+ *   b1, b3  [E][d_ff]   (gate, up)
+ *   b2      [E][d]      (down)                                              */
+typedef struct {
+  const void* b1;
+  const void* b3;
+  const void* b2;
+} moe_expert_bias;
+
 /* Bytes of workspace moe_forward and moe_block_forward need (256-byte
  * aligned sub-buffers: routing, permutation, h [T*k][d_ff] in wt, y_sorted
  * [T*k][d] fp32, and for the block form the normalised input).  Returns 0
@@ -113,8 +128,10 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
 
 /* Experts: for every row r of expert e (in dispatch order),
  *   y_sorted[r] = (SiLU(x[t] W1_e^T) * (x[t] W3_e^T)) W2_e^T,  t = sorted_token[r]
- * ("Прямой проход в формулах", MoE equation, the SwiGLU term).
+ * ("Прямой проход в формулах", MoE equation, the SwiGLU term), plus the
+ * expert's Linear biases when expert_bias gives them (see moe_expert_bias).
  *   x             [T][d] in act;  w1, w3 [E][d_ff][d], w2 [E][d][d_ff] in wt
+ *   expert_bias   NULL or biases (see above)
  *   y_sorted      [T*k][d] fp32 output
  *   ws            >= moe_expert_ffn_workspace_size(shape) bytes
  * Small T (<= 64, bf16) runs the weight-streaming path that reads each
@@ -122,7 +139,8 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx,
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x,
                           const int32_t* expert_offsets, const int32_t* sorted_token,
                           const void* w1, const void* w3, const void* w2,
-                          float* y_sorted, void* ws, size_t ws_bytes, void* stream);
+                          const moe_expert_bias* expert_bias, float* y_sorted,
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: y[t] = sum_s topk_w[t][s] * y_sorted[inv_pos[t][s]] (+ residual[t]),
  * in fp32, rounded once to act ("Алгоритм", the weighted index-add, done as
@@ -134,12 +152,14 @@ moe_status moe_combine(const moe_shape* shape, const float* y_sorted,
                        const void* residual, void* y, void* stream);
 
 /* The whole layer: route -> dispatch -> experts -> combine on one stream.
+ *   bias         router bias [E] fp32 or NULL (as in moe_route)
+ *   expert_bias  NULL or the experts' Linear biases (moe_expert_bias)
  *   y [T][d] in act output (must not alias x)
  *   ws >= moe_workspace_size(shape) bytes                                   */
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate,
                        const float* bias, const void* w1, const void* w3,
-                       const void* w2, void* y, void* ws, size_t ws_bytes,
-                       void* stream);
+                       const void* w2, const moe_expert_bias* expert_bias,
+                       void* y, void* ws, size_t ws_bytes, void* stream);
 
 /* One pre-norm residual MoE sublayer ("Прямой проход в формулах", block
  * equation H = U + MoE(RMSNorm_2(U)); RMSNorm(z) = z / sqrt(mean z^2 + eps)
@@ -150,6 +170,7 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
 moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma,
                              float eps, const float* w_gate, const float* bias,
                              const void* w1, const void* w3, const void* w2,
+                             const moe_expert_bias* expert_bias,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* Router load-balancing loss ("Mixtral" page, section "Load-balancing

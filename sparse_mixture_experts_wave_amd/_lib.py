@@ -27,8 +27,13 @@ class MoEShape(ctypes.Structure):
     ]
 
 
+class MoEExpertBias(ctypes.Structure):
+    _fields_ = [("b1", ctypes.c_void_p), ("b3", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
 _vp = ctypes.c_void_p
 _sp = ctypes.POINTER(MoEShape)
+_bp = ctypes.POINTER(MoEExpertBias)
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -36,10 +41,10 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_sp]),
     "moe_route": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_dispatch": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
-    "moe_expert_ffn": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "moe_expert_ffn": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _bp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "moe_forward": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
-    "moe_block_forward": (ctypes.c_int, [_sp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
+    "moe_forward": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _bp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "moe_block_forward": (ctypes.c_int, [_sp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _bp, _vp,
                                          ctypes.c_size_t, _vp]),
     "moe_aux_loss": (ctypes.c_int, [_sp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp]),
     "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),

@@ -1,9 +1,10 @@
 // Prefill-regime expert FFN: grouped bf16 GEMM on the MFMA units.
 //
-//   up   (GATED): h[r]        = SiLU(x[t] W1_e^T) * (x[t] W3_e^T),  t = sorted_token[r]
-//   down        : y_sorted[r] = h[r] W2_e^T
+//   up   (GATED): h[r]        = SiLU(x[t] W1_e^T + b1_e) * (x[t] W3_e^T + b3_e),  t = sorted_token[r]
+//   down        : y_sorted[r] = h[r] W2_e^T + b2_e
 // ("Mixtral" textbook page, "Прямой проход в формулах", MoE equation, expert
-// term; w1 = gate, w3 = up, w2 = down per the page's HuggingFace mapping.)
+// term; w1 = gate, w3 = up, w2 = down per the page's HuggingFace mapping; the
+// Linear biases are optional, section "Конфигурация", key `bias`.)
 //
 // Tiling.  One 512-thread workgroup computes a 256-row x 256-column tile of
 // (rows of one expert) x (weight rows).  For the up projection the 256 weight
@@ -273,7 +274,8 @@ template <bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, void* __restrict__ out, int N, int K, int NT) {
+    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int NT) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;  // output columns per tile
   Tile t;
   if (!map_tile(offsets, E, NT, COLS, blockIdx.x, t)) return;
@@ -327,7 +329,15 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     mainloop<GATED, false>(cs, K, t.rows, acc);
 
   // Epilogue.  32x32 accumulator layout: lane holds column lane%32 and rows
-  // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.
+  // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Bias of each of the
+  // lane's columns (gated: the W1 and W3 bias of its one column).
+  float bb[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = GATED ? t.n0 + wn * 32 + (lane & 31) : t.n0 + wn * 64 + nb * 32 + (lane & 31);
+    const uint16_t* bsrc = (GATED && nb == 1) ? bias1 : bias0;
+    bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
+  }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -337,12 +347,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
       const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
       if constexpr (GATED) {
         const int n = t.n0 + wn * 32 + (lane & 31);
-        if (n < N) static_cast<uint16_t*>(out)[row + n] = f32_to_bf16(silu_fast(acc[mi][0][v]) * acc[mi][1][v]);
+        if (n < N)
+          static_cast<uint16_t*>(out)[row + n] = f32_to_bf16(silu_fast(acc[mi][0][v] + bb[0]) * (acc[mi][1][v] + bb[1]));
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
-          if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v];
+          if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v] + bb[nb];
         }
       }
     }
@@ -350,26 +361,30 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
 
 template <bool GATED>
 hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const uint16_t* B0,
-                  const uint16_t* B1, void* out, int64_t rows, int N, int K, int E, hipStream_t s) {
+                  const uint16_t* B1, const uint16_t* bias0, const uint16_t* bias1, void* out, int64_t rows,
+                  int N, int K, int E, hipStream_t s) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const int NT = (N + COLS - 1) / COLS;
   // Upper bound on the row tiles: sum_e ceil(n_e / BM) <= ceil(rows / BM) + E.
   const int64_t tiles = ((rows + BM - 1) / BM + E) * NT;
-  gemm_bf16_kernel<GATED><<<static_cast<unsigned>(tiles), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, out, N, K, NT);
+  gemm_bf16_kernel<GATED><<<static_cast<unsigned>(tiles), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0, bias1,
+                                                                         out, N, K, NT);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
-                               const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int k, int d,
-                               int d_ff, int E, hipStream_t stream) {
-  return launch<true>(x, sorted_token, offsets, w1, w3, h, T * k, d_ff, d, E, stream);
+                               const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
+                               const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
+                               hipStream_t stream) {
+  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, T * k, d_ff, d, E, stream);
 }
 
-hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2, float* y_sorted,
-                                 int64_t T, int k, int d, int d_ff, int E, hipStream_t stream) {
-  return launch<false>(h, nullptr, offsets, w2, nullptr, y_sorted, T * k, d, d_ff, E, stream);
+hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
+                                 const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
+                                 int E, hipStream_t stream) {
+  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, T * k, d, d_ff, E, stream);
 }
 
 }  // namespace moe

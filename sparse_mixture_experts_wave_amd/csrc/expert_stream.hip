@@ -13,7 +13,8 @@
 // four instructions of a step cover 256 contiguous bytes per row.  The
 // expert's rows (tokens) are the MFMA's A operand, 16 per M-block, MB blocks
 // per pass.  Partial sums of the KS waves are reduced through LDS by wave 0,
-// which applies the SiLU * up epilogue (up) or stores fp32 (down).
+// which adds the optional Linear biases ("Конфигурация", key `bias`) and
+// applies the SiLU * up epilogue (up) or stores fp32 (down).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -24,7 +25,8 @@ template <int MB, int NG, int KS, bool GATED>
 __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, void* __restrict__ out, int N, int K, int E) {
+    const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int E) {
   constexpr int NACC = MB * NG * (GATED ? 2 : 1);
   __shared__ f32x4 red[KS - 1][NACC][64];
 
@@ -136,6 +138,13 @@ __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
             }
         }
         // 16x16 accumulator layout: lane holds column lane%16, rows 4*(lane/16)+v.
+        float bb0[NG], bb1[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const int64_t bi = static_cast<int64_t>(e) * N + n0 + 16 * g + m;
+          bb0[g] = bias0 ? bf16_to_f32(bias0[bi]) : 0.f;
+          bb1[g] = (GATED && bias1) ? bf16_to_f32(bias1[bi]) : 0.f;
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -146,9 +155,10 @@ __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
               if (r < n_e) {
                 const int64_t o = static_cast<int64_t>(lo + r) * N + n0 + 16 * g + m;
                 if constexpr (GATED)
-                  static_cast<uint16_t*>(out)[o] = f32_to_bf16(silu_fast(acc0[mb][g][v]) * acc1[mb][g][v]);
+                  static_cast<uint16_t*>(out)[o] =
+                      f32_to_bf16(silu_fast(acc0[mb][g][v] + bb0[g]) * (acc1[mb][g][v] + bb1[g]));
                 else
-                  static_cast<float*>(out)[o] = acc0[mb][g][v];
+                  static_cast<float*>(out)[o] = acc0[mb][g][v] + bb0[g];
               }
             }
       }
@@ -157,24 +167,32 @@ __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
   }
 }
 
+// Weights, biases and output of one projection.
+struct Proj {
+  const uint16_t* B0;
+  const uint16_t* B1;
+  const uint16_t* bias0;
+  const uint16_t* bias1;
+  void* out;
+};
+
 template <int MB, int NG, int KS, bool GATED>
-hipError_t launch_cfg(const uint16_t* A, const int32_t* gather, const int32_t* offsets,
-                      const uint16_t* B0, const uint16_t* B1, void* out, int N, int K, int E,
-                      int grid, hipStream_t s) {
+hipError_t launch_cfg(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const Proj& p, int N,
+                      int K, int E, int grid, hipStream_t s) {
   const int items = E * (N / (16 * NG));
   const int blocks = grid > 0 && grid < items ? grid : items;
-  stream_ffn_bf16_kernel<MB, NG, KS, GATED><<<blocks, 64 * KS, 0, s>>>(A, gather, offsets, B0, B1, out, N, K, E);
+  stream_ffn_bf16_kernel<MB, NG, KS, GATED><<<blocks, 64 * KS, 0, s>>>(A, gather, offsets, p.B0, p.B1, p.bias0,
+                                                                        p.bias1, p.out, N, K, E);
   return hipGetLastError();
 }
 
 template <int NG, int KS, bool GATED>
-hipError_t launch_mb(int64_t T, const uint16_t* A, const int32_t* gather, const int32_t* offsets,
-                     const uint16_t* B0, const uint16_t* B1, void* out, int N, int K, int E, int grid,
-                     hipStream_t s) {
+hipError_t launch_mb(int64_t T, const uint16_t* A, const int32_t* gather, const int32_t* offsets, const Proj& p,
+                     int N, int K, int E, int grid, hipStream_t s) {
   // n_e <= T: the experts of one token are distinct.
-  if (T <= 16) return launch_cfg<1, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
-  if (T <= 32) return launch_cfg<2, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
-  return launch_cfg<4, NG, KS, GATED>(A, gather, offsets, B0, B1, out, N, K, E, grid, s);
+  if (T <= 16) return launch_cfg<1, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
+  if (T <= 32) return launch_cfg<2, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
+  return launch_cfg<4, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
 }
 
 // Workgroups of the grid-stride loop (8 per CU on 256 CUs): enough bytes in
@@ -188,20 +206,23 @@ bool stream_supported(int64_t T, int d, int d_ff) {
 }
 
 hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
-                                 const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
-                                 int d_ff, int E, hipStream_t stream) {
+                                 const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
+                                 const uint16_t* b3, uint16_t* h, int64_t T, int d, int d_ff, int E,
+                                 hipStream_t stream) {
+  const Proj p{w1, w3, b1, b3, h};
   // Few tokens touch few experts: narrower work items (16 columns) keep every
   // workgroup busy; the K split doubles when it divides evenly.
   if (T <= 4 && d % 1024 == 0)
-    return launch_mb<1, 8, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, kStreamGrid, stream);
-  return launch_mb<2, 4, true>(T, x, sorted_token, offsets, w1, w3, h, d_ff, d, E, kStreamGrid, stream);
+    return launch_mb<1, 8, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
+  return launch_mb<2, 4, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
 }
 
-hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2, float* y_sorted,
-                                   int64_t T, int d, int d_ff, int E, hipStream_t stream) {
-  if (T <= 4)
-    return launch_mb<1, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, kStreamGrid, stream);
-  return launch_mb<2, 4, false>(T, h, nullptr, offsets, w2, nullptr, y_sorted, d, d_ff, E, kStreamGrid, stream);
+hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
+                                   const uint16_t* b2, float* y_sorted, int64_t T, int d, int d_ff, int E,
+                                   hipStream_t stream) {
+  const Proj p{w2, nullptr, b2, nullptr, y_sorted};
+  if (T <= 4) return launch_mb<1, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
+  return launch_mb<2, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
 }
 
 }  // namespace moe

@@ -21,24 +21,26 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E,
                            hipStream_t stream);
 
 // Expert SwiGLU FFN over the dispatched rows, bf16 weights/activations, in two
-// launches: up (h = SiLU(x W1^T) * (x W3^T), [T*k][d_ff] bf16) and down
-// (y_sorted = h W2^T, [T*k][d] fp32).  Small T streams the weights.
+// launches: up (h = SiLU(x W1^T + b1) * (x W3^T + b3), [T*k][d_ff] bf16) and
+// down (y_sorted = h W2^T + b2, [T*k][d] fp32).  Each per-expert Linear bias
+// ([E][d_ff] or [E][d], weight dtype) may be null.  Small T streams the weights.
 hipError_t launch_expert_up_bf16(const uint16_t* x, const int32_t* expert_offsets,
                                  const int32_t* sorted_token, const uint16_t* w1,
-                                 const uint16_t* w3, uint16_t* h, int64_t T, int k, int d,
-                                 int d_ff, int E, hipStream_t stream);
+                                 const uint16_t* w3, const uint16_t* b1, const uint16_t* b3,
+                                 uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
+                                 hipStream_t stream);
 hipError_t launch_expert_down_bf16(const uint16_t* h, const int32_t* expert_offsets,
-                                   const uint16_t* w2, float* y_sorted, int64_t T, int k, int d,
-                                   int d_ff, int E, hipStream_t stream);
+                                   const uint16_t* w2, const uint16_t* b2, float* y_sorted, int64_t T,
+                                   int k, int d, int d_ff, int E, hipStream_t stream);
 
 // Same in fp32 (h is [T*k][d_ff] fp32).
 hipError_t launch_expert_up_f32(const float* x, const int32_t* expert_offsets,
                                 const int32_t* sorted_token, const float* w1, const float* w3,
-                                float* h, int64_t T, int k, int d, int d_ff, int E,
-                                hipStream_t stream);
+                                const float* b1, const float* b3, float* h, int64_t T, int k, int d,
+                                int d_ff, int E, hipStream_t stream);
 hipError_t launch_expert_down_f32(const float* h, const int32_t* expert_offsets, const float* w2,
-                                  float* y_sorted, int64_t T, int k, int d, int d_ff, int E,
-                                  hipStream_t stream);
+                                  const float* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
+                                  int E, hipStream_t stream);
 
 // Weighted gather-combine (+ optional residual), output in the activation dtype.
 hipError_t launch_combine(const float* y_sorted, const int32_t* inv_pos, const float* topk_w,
@@ -49,19 +51,21 @@ hipError_t launch_combine(const float* y_sorted, const int32_t* inv_pos, const f
 // launchers above when stream_supported(T, d, d_ff).
 bool stream_supported(int64_t T, int d, int d_ff);
 hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
-                                 const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int d,
-                                 int d_ff, int E, hipStream_t stream);
+                                 const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
+                                 const uint16_t* b3, uint16_t* h, int64_t T, int d, int d_ff, int E,
+                                 hipStream_t stream);
 hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
-                                   float* y_sorted, int64_t T, int d, int d_ff, int E,
-                                   hipStream_t stream);
+                                   const uint16_t* b2, float* y_sorted, int64_t T, int d, int d_ff,
+                                   int E, hipStream_t stream);
 
 // Prefill-regime grouped MFMA GEMMs (expert_gemm.hip).
 hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
-                               const uint16_t* w1, const uint16_t* w3, uint16_t* h, int64_t T, int k,
-                               int d, int d_ff, int E, hipStream_t stream);
+                               const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
+                               const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
+                               hipStream_t stream);
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
-                                 float* y_sorted, int64_t T, int k, int d, int d_ff, int E,
-                                 hipStream_t stream);
+                                 const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
+                                 int E, hipStream_t stream);
 
 // Router load-balancing loss over [layers][T][E] logits (aux_loss.hip).
 int aux_loss_max_k();

@@ -137,34 +137,50 @@ moe_status mark(int point, void* stream) {
   return hip_status(hipEventRecord(g_events[point], hs(stream)), "timing event record");
 }
 
+// Optional expert biases: every pointer may be NULL, and so may the struct.
+moe_status check_bias(const moe_expert_bias* eb) {
+  if (eb == nullptr) return MOE_OK;
+  MOE_TRY(optional(eb->b1, "expert_bias->b1"));
+  MOE_TRY(optional(eb->b3, "expert_bias->b3"));
+  return optional(eb->b2, "expert_bias->b2");
+}
+
 moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const int32_t* st,
-                   const void* w1, const void* w3, const void* w2, float* y_sorted, void* h,
-                   void* stream, bool timed) {
+                   const void* w1, const void* w3, const void* w2, const moe_expert_bias* eb, float* y_sorted,
+                   void* h, void* stream, bool timed) {
+  const void* b1 = eb ? eb->b1 : nullptr;
+  const void* b3 = eb ? eb->b3 : nullptr;
+  const void* b2 = eb ? eb->b2 : nullptr;
   hipError_t err;
   if (s->wt == MOE_BF16) {
     err = moe::launch_expert_up_bf16(static_cast<const uint16_t*>(x), off, st, static_cast<const uint16_t*>(w1),
-                                     static_cast<const uint16_t*>(w3), static_cast<uint16_t*>(h), s->T, s->k,
+                                     static_cast<const uint16_t*>(w3), static_cast<const uint16_t*>(b1),
+                                     static_cast<const uint16_t*>(b3), static_cast<uint16_t*>(h), s->T, s->k,
                                      s->d, s->d_ff, s->E, hs(stream));
   } else {
     err = moe::launch_expert_up_f32(static_cast<const float*>(x), off, st, static_cast<const float*>(w1),
-                                    static_cast<const float*>(w3), static_cast<float*>(h), s->T, s->k, s->d,
+                                    static_cast<const float*>(w3), static_cast<const float*>(b1),
+                                    static_cast<const float*>(b3), static_cast<float*>(h), s->T, s->k, s->d,
                                     s->d_ff, s->E, hs(stream));
   }
   MOE_TRY(hip_status(err, "expert up launch"));
   if (timed) MOE_TRY(mark(3, stream));
   if (s->wt == MOE_BF16) {
     err = moe::launch_expert_down_bf16(static_cast<const uint16_t*>(h), off, static_cast<const uint16_t*>(w2),
-                                       y_sorted, s->T, s->k, s->d, s->d_ff, s->E, hs(stream));
+                                       static_cast<const uint16_t*>(b2), y_sorted, s->T, s->k, s->d, s->d_ff,
+                                       s->E, hs(stream));
   } else {
-    err = moe::launch_expert_down_f32(static_cast<const float*>(h), off, static_cast<const float*>(w2), y_sorted,
-                                      s->T, s->k, s->d, s->d_ff, s->E, hs(stream));
+    err = moe::launch_expert_down_f32(static_cast<const float*>(h), off, static_cast<const float*>(w2),
+                                      static_cast<const float*>(b2), y_sorted, s->T, s->k, s->d, s->d_ff, s->E,
+                                      hs(stream));
   }
   return hip_status(err, "expert down launch");
 }
 
 moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, const float* bias,
-                        const void* w1, const void* w3, const void* w2, void* y, const void* residual,
-                        const float* gamma, float eps, void* ws, size_t ws_bytes, void* stream) {
+                        const void* w1, const void* w3, const void* w2, const moe_expert_bias* eb, void* y,
+                        const void* residual, const float* gamma, float eps, void* ws, size_t ws_bytes,
+                        void* stream) {
   const bool block = gamma != nullptr;
   const Layout L = layout(s, block);
   if (ws_bytes < L.total)
@@ -187,7 +203,7 @@ moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, 
   MOE_TRY(mark(1, stream));
   MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
   MOE_TRY(mark(2, stream));
-  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, ys, h, stream, true));
+  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, stream, true));
   MOE_TRY(mark(4, stream));
   MOE_TRY(hip_status(moe::launch_combine(ys, inv, w, residual, y, s->act == MOE_BF16, s->T, s->k, s->d, hs(stream)),
                      "combine launch"));
@@ -241,7 +257,8 @@ moe_status moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t
 
 moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* expert_offsets,
                           const int32_t* sorted_token, const void* w1, const void* w3, const void* w2,
-                          float* y_sorted, void* ws, size_t ws_bytes, void* stream) {
+                          const moe_expert_bias* expert_bias, float* y_sorted, void* ws, size_t ws_bytes,
+                          void* stream) {
   MOE_TRY(check_shape(shape));
   if (shape->T == 0) return ok();
   MOE_TRY(need(x, "x"));
@@ -250,11 +267,12 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   MOE_TRY(need(w1, "w1"));
   MOE_TRY(need(w3, "w3"));
   MOE_TRY(need(w2, "w2"));
+  MOE_TRY(check_bias(expert_bias));
   MOE_TRY(need(y_sorted, "y_sorted"));
   MOE_TRY(need(ws, "ws"));
   if (ws_bytes < ffn_ws(shape))
     return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, ffn_ws(shape));
-  return run_ffn(shape, x, expert_offsets, sorted_token, w1, w3, w2, y_sorted, ws, stream, false);
+  return run_ffn(shape, x, expert_offsets, sorted_token, w1, w3, w2, expert_bias, y_sorted, ws, stream, false);
 }
 
 moe_status moe_combine(const moe_shape* shape, const float* y_sorted, const int32_t* inv_pos,
@@ -272,8 +290,8 @@ moe_status moe_combine(const moe_shape* shape, const float* y_sorted, const int3
 }
 
 moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
-                       const void* w1, const void* w3, const void* w2, void* y, void* ws, size_t ws_bytes,
-                       void* stream) {
+                       const void* w1, const void* w3, const void* w2, const moe_expert_bias* expert_bias,
+                       void* y, void* ws, size_t ws_bytes, void* stream) {
   MOE_TRY(check_shape(shape));
   if (shape->T == 0) return ok();
   MOE_TRY(need(x, "x"));
@@ -282,15 +300,18 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
   MOE_TRY(need(w1, "w1"));
   MOE_TRY(need(w3, "w3"));
   MOE_TRY(need(w2, "w2"));
+  MOE_TRY(check_bias(expert_bias));
   MOE_TRY(need(y, "y"));
   if (x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
   MOE_TRY(need(ws, "ws"));
-  return forward_impl(shape, x, w_gate, bias, w1, w3, w2, y, nullptr, nullptr, 0.f, ws, ws_bytes, stream);
+  return forward_impl(shape, x, w_gate, bias, w1, w3, w2, expert_bias, y, nullptr, nullptr, 0.f, ws, ws_bytes,
+                      stream);
 }
 
 moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma, float eps,
                              const float* w_gate, const float* bias, const void* w1, const void* w3,
-                             const void* w2, void* ws, size_t ws_bytes, void* stream) {
+                             const void* w2, const moe_expert_bias* expert_bias, void* ws, size_t ws_bytes,
+                             void* stream) {
   MOE_TRY(check_shape(shape));
   if (!(eps > 0.f)) return fail(MOE_ERR_INVALID_ARG, "eps = %g must be > 0", static_cast<double>(eps));
   if (shape->T == 0) return ok();
@@ -301,9 +322,10 @@ moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float*
   MOE_TRY(need(w1, "w1"));
   MOE_TRY(need(w3, "w3"));
   MOE_TRY(need(w2, "w2"));
+  MOE_TRY(check_bias(expert_bias));
   MOE_TRY(need(ws, "ws"));
-  return forward_impl(shape, h_inout, w_gate, bias, w1, w3, w2, h_inout, h_inout, gamma, eps, ws, ws_bytes,
-                      stream);
+  return forward_impl(shape, h_inout, w_gate, bias, w1, w3, w2, expert_bias, h_inout, h_inout, gamma, eps, ws,
+                      ws_bytes, stream);
 }
 
 moe_status moe_aux_loss(const moe_shape* shape, const float* logits, int32_t num_layers,

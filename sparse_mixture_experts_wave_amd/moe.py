@@ -55,6 +55,19 @@ def expert_ffn_workspace_size(shape: _lib.MoEShape) -> int:
     return int(_lib.load().moe_expert_ffn_workspace_size(ctypes.byref(shape)))
 
 
+def _expert_bias(b1: Optional[torch.Tensor], b3: Optional[torch.Tensor], b2: Optional[torch.Tensor],
+                 E: int, d: int, d_ff: int, wt: torch.dtype):
+    """Pointer to a moe_expert_bias struct, or None when no bias is given."""
+    if b1 is None and b3 is None and b2 is None:
+        return None
+    for t, name, n in ((b1, "b1", d_ff), (b3, "b3", d_ff), (b2, "b2", d)):
+        if t is not None:
+            _gpu(t, name)
+            if t.dtype != wt or tuple(t.shape) != (E, n):
+                raise ValueError(f"{name} must be [{E}, {n}] in the weight dtype {wt}")
+    return ctypes.byref(_lib.MoEExpertBias(_p(b1), _p(b3), _p(b2)))
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -98,8 +111,11 @@ def moe_dispatch(topk_idx: torch.Tensor, E: int, d: int = 64):
 
 def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_token: torch.Tensor,
                    w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, k: int = 2,
-                   y_sorted: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Expert SwiGLU on every dispatched row -> y_sorted [T*k, d] fp32."""
+                   y_sorted: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
+                   b3: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Expert SwiGLU on every dispatched row -> y_sorted [T*k, d] fp32.
+
+    b1, b3 [E, d_ff] and b2 [E, d] are the experts' optional Linear biases."""
     x, w1, w3, w2 = _gpu(x, "x"), _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
     T, d = x.shape
     E, d_ff, _ = w1.shape
@@ -109,8 +125,9 @@ def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_token: 
     if y_sorted is None:
         y_sorted = torch.empty((max(T * k, 1), d), dtype=torch.float32, device=x.device)
     ws = _ws(expert_ffn_workspace_size(shape), x.device)
+    eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
     _lib.check(_lib.load().moe_expert_ffn(ctypes.byref(shape), _p(x), _p(expert_offsets), _p(sorted_token),
-                                          _p(w1), _p(w3), _p(w2), _p(y_sorted), _p(ws), ws.numel(),
+                                          _p(w1), _p(w3), _p(w2), eb, _p(y_sorted), _p(ws), ws.numel(),
                                           _stream(x)))
     return y_sorted[:T * k]
 
@@ -133,8 +150,11 @@ def moe_combine(y_sorted: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Ten
 
 def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor], w1: torch.Tensor,
                 w3: torch.Tensor, w2: torch.Tensor, k: int = 2, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The whole layer y = sum_{i in Top2} softmax_i * SwiGLU_i(x) -> [T, d] in x.dtype."""
+                workspace: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
+                b3: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer y = sum_{i in Top2} softmax_i * SwiGLU_i(x) -> [T, d] in x.dtype.
+
+    bias is the router's; b1, b3 [E, d_ff] and b2 [E, d] the experts' optional Linear biases."""
     x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
     w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
     T, d = x.shape
@@ -144,14 +164,16 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tens
         out = torch.empty_like(x)
     if workspace is None:
         workspace = _ws(workspace_size(shape), x.device)
+    eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
     _lib.check(_lib.load().moe_forward(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3), _p(w2),
-                                       _p(out), _p(workspace), workspace.numel(), _stream(x)))
+                                       eb, _p(out), _p(workspace), workspace.numel(), _stream(x)))
     return out
 
 
 def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: torch.Tensor,
                       bias: Optional[torch.Tensor], w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
-                      k: int = 2, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      k: int = 2, workspace: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
+                      b3: Optional[torch.Tensor] = None, b2: Optional[torch.Tensor] = None) -> torch.Tensor:
     """In place: h <- h + MoE(RMSNorm(h) * gamma).  Returns h."""
     h, gamma, w_gate, bias = _gpu(h, "h"), _gpu(gamma, "gamma"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
     w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
@@ -160,9 +182,10 @@ def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: 
     shape = make_shape(T, d, d_ff, E, k, h.dtype, w1.dtype)
     if workspace is None:
         workspace = _ws(workspace_size(shape), h.device)
+    eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
     _lib.check(_lib.load().moe_block_forward(ctypes.byref(shape), _p(h), _p(gamma), float(eps), _p(w_gate),
-                                             _p(bias), _p(w1), _p(w3), _p(w2), _p(workspace), workspace.numel(),
-                                             _stream(h)))
+                                             _p(bias), _p(w1), _p(w3), _p(w2), eb, _p(workspace),
+                                             workspace.numel(), _stream(h)))
     return h
 
 

@@ -17,6 +17,8 @@ Storage layout (nn.Linear convention, reduction dimension contiguous):
   w1     [E, d_ff, d]      gate projection  (HF name w1)
   w3     [E, d_ff, d]      up projection    (HF name w3)
   w2     [E, d, d_ff]      down projection  (HF name w2)
+  b1, b3 [E, d_ff], b2 [E, d]   optional expert Linear biases (weight dtype),
+         drawn N(0, expert_bias_std) when that is nonzero, else None
 bf16 tensors are returned as uint16 bit patterns, rounded from fp32 to
 nearest-even.  Nothing here computes any part of the layer.
 """
@@ -28,7 +30,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-TENSOR_IDS = {"x": 0, "w_gate": 1, "w1": 2, "w3": 3, "w2": 4}
+TENSOR_IDS = {"x": 0, "w_gate": 1, "w1": 2, "w3": 3, "w2": 4, "b1": 6, "b3": 7, "b2": 8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -44,6 +46,7 @@ class MoEConfig:
     x_unit_rms: bool = False       # rows of x scaled onto the sphere of radius sqrt(d)
     wg_std: float = 0.02           # std of the router weights
     bias: Optional[str] = None     # None or "zipf1.2"
+    expert_bias_std: float = 0.0   # 0: experts without Linear biases (Mixtral 8x7B)
     layers: int = 1
     description: str = ""
 
@@ -146,6 +149,9 @@ def generate(cfg: MoEConfig, layer: int = 0, seed: int = 0,
         out["w3"] = _expert_stack(_rng(seed, cfg, layer, "w3"), cfg.E, cfg.d_ff, cfg.d, cfg.w1_std, cfg.dtype)
     if "w2" in tensors:
         out["w2"] = _expert_stack(_rng(seed, cfg, layer, "w2"), cfg.E, cfg.d, cfg.d_ff, cfg.w2_std, cfg.dtype)
+    for name, cols in (("b1", cfg.d_ff), ("b3", cfg.d_ff), ("b2", cfg.d)):
+        out[name] = (_store(_normal(_rng(seed, cfg, layer, name), (cfg.E, cols), cfg.expert_bias_std), cfg.dtype)
+                     if cfg.expert_bias_std > 0 else None)
     return out
 
 

@@ -78,9 +78,9 @@ def test_zero_tokens_is_a_no_op(lib):
     s = shape(T=0)
     assert route(lib, s) == _lib.MOE_OK
     assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None) == _lib.MOE_OK
-    assert lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x20000),
+    assert lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x20000),
                            None, 0, None) == _lib.MOE_OK
-    assert lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+    assert lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0,
                               None) == _lib.MOE_OK
 
 
@@ -98,22 +98,37 @@ def test_workspace_sizes(lib):
 
 def test_workspace_too_small_is_rejected(lib):
     s = shape(T=16)
-    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.c_void_p(0x20000),
+    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x20000),
                          FAKE, 1024, None)
     assert st == _lib.MOE_ERR_INVALID_ARG and b"workspace" in lib.moe_last_error()
-    st = lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    st = lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, None)
     assert st == _lib.MOE_ERR_INVALID_ARG
 
 
 def test_forward_rejects_aliased_output(lib):
     s = shape(T=16)
-    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None)
     assert st == _lib.MOE_ERR_INVALID_ARG and b"alias" in lib.moe_last_error()
+
+
+def test_expert_bias_pointers_are_validated(lib):
+    s = shape(T=16)
+    bad = _lib.MoEExpertBias(None, MISALIGNED, None)
+    st = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, ctypes.byref(bad),
+                         ctypes.c_void_p(0x20000), FAKE, 1 << 40, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"expert_bias->b3" in lib.moe_last_error()
+    st = lib.moe_expert_ffn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE,
+                            1 << 40, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"expert_bias->b3" in lib.moe_last_error()
+    st = lib.moe_block_forward(ctypes.byref(s), FAKE, FAKE, 1e-5, FAKE, None, FAKE, FAKE, FAKE, ctypes.byref(bad),
+                               FAKE, 1 << 40, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"expert_bias->b3" in lib.moe_last_error()
 
 
 def test_block_forward_validates_eps(lib):
     s = shape(T=16)
-    st = lib.moe_block_forward(ctypes.byref(s), FAKE, FAKE, 0.0, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    st = lib.moe_block_forward(ctypes.byref(s), FAKE, FAKE, 0.0, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                               None)
     assert st == _lib.MOE_ERR_INVALID_ARG and b"eps" in lib.moe_last_error()
 
 

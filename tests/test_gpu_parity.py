@@ -407,3 +407,90 @@ def test_forward_general_k(T, d, d_ff, k):
     gaps = np.diff(-s, axis=1)
     clear = np.all(gaps[:, :k] > 1e-4, axis=1) if k < 8 else np.ones(T, bool)
     assert max_rel_err(y, y_ref, clear) <= BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# expert Linear biases ("Mixtral" page, "Конфигурация", key `bias`)
+# ---------------------------------------------------------------------------
+def _eb(inp, which="b1b3b2"):
+    return tuple(inp[n] if n in which else None for n in ("b1", "b3", "b2"))
+
+
+def _eb_dev(eb):
+    return dict(zip(("b1", "b3", "b2"), (to_dev(b) for b in eb)))
+
+
+@pytest.mark.parametrize("T,d,d_ff,dtype,path,which", [
+    (64, 128, 256, "f32", "gemm", "b1b3b2"),
+    (300, 192, 320, "bf16", "gemm", "b1b3b2"),
+    (1000, 256, 384, "bf16", "gemm", "b3"),
+    (16, 512, 1024, "bf16", "stream", "b1b3b2"),
+    (3, 1024, 1024, "bf16", "stream", "b1b3b2"),
+    (40, 512, 512, "bf16", "stream", "b2"),
+])
+def test_expert_ffn_with_biases(T, d, d_ff, dtype, path, which):
+    say(f"expert_ffn biases T={T} d={d} d_ff={d_ff} {dtype} {path} {which}")
+    cfg = small("ffnb", T, d, d_ff, dtype=dtype).with_(expert_bias_std=0.1)
+    inp = generate(cfg)
+    g, idx, w = oracle.route_ref(inp["x"], inp["w_gate"], None)
+    off, st, inv = oracle.dispatch_ref(idx, 8)
+    eb = _eb(inp, which)
+    ref = oracle.expert_rows_ref(inp["x"], st, off, inp["w1"], inp["w3"], inp["w2"], eb=eb)
+    ys = moe.moe_expert_ffn(to_dev(inp["x"]), to_dev(off), to_dev(st), to_dev(inp["w1"]), to_dev(inp["w3"]),
+                            to_dev(inp["w2"]), **_eb_dev(eb))
+    torch.cuda.synchronize()
+    err = max_rel_err(to_host(ys), ref)
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL), err
+
+
+@pytest.mark.parametrize("cfg", [
+    small("fwd_bias_bf16", 1000, 256, 384),
+    small("fwd_bias_decode", 16, 512, 1024),
+    small("fwd_bias_t1", 1, 512, 512),
+    small("fwd_bias_fp32", 333, 192, 256, dtype="f32"),
+], ids=lambda c: c.name)
+def test_forward_with_expert_biases(cfg):
+    say(f"forward biases {cfg.name}")
+    cfg = cfg.with_(expert_bias_std=0.1)
+    inp = generate(cfg)
+    eb = _eb(inp)
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(inp["x"], inp["w_gate"], None, inp["w1"], inp["w3"],
+                                                        inp["w2"], eb=eb)
+    dv = {key: to_dev(v) for key, v in inp.items()}
+    y = moe.moe_forward(dv["x"], dv["w_gate"], None, dv["w1"], dv["w3"], dv["w2"], **_eb_dev(eb))
+    torch.cuda.synchronize()
+    clear, _ = clear_tokens(g)
+    assert max_rel_err(to_host(y), y_ref, clear) <= (F32_TOL if cfg.dtype == "f32" else BF16_TOL)
+
+
+def test_zero_expert_biases_equal_none():
+    say("forward zero biases == none")
+    cfg = small("fwd_zero_bias", 300, 256, 384)
+    inp = generate(cfg)
+    dv = {key: to_dev(v) for key, v in inp.items()}
+    z = lambda n: torch.zeros((8, n), dtype=torch.bfloat16, device=dv["x"].device)
+    y0 = moe.moe_forward(dv["x"], dv["w_gate"], None, dv["w1"], dv["w3"], dv["w2"])
+    y1 = moe.moe_forward(dv["x"], dv["w_gate"], None, dv["w1"], dv["w3"], dv["w2"], b1=z(384), b3=z(384),
+                         b2=z(256))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_block_forward_with_expert_biases():
+    say("block forward biases")
+    cfg = small("blockb", 300, 256, 384).with_(expert_bias_std=0.1)
+    inp = generate(cfg)
+    eb = _eb(inp)
+    h_in = inp["x"].copy()
+    dv_h = to_dev(h_in)
+    gamma = np.ones(cfg.d, np.float32)
+    moe.moe_block_forward(dv_h, to_dev(gamma), 1e-5, to_dev(inp["w_gate"]), None, to_dev(inp["w1"]),
+                          to_dev(inp["w3"]), to_dev(inp["w2"]), **_eb_dev(eb))
+    torch.cuda.synchronize()
+    h_out = widen_host(to_host(dv_h))
+    ref, u, (g, idx, w) = oracle.block_forward_ref(h_in, gamma, 1e-5, inp["w_gate"], None, inp["w1"], inp["w3"],
+                                                   inp["w2"], eb=eb)
+    y_ref = ref - widen_host(h_in)
+    clear, _ = clear_tokens(g)
+    tol = BF16_TOL * np.max(np.abs(y_ref)) + 2 ** -8 * np.max(np.abs(ref))
+    assert np.max(np.abs(h_out[clear] - ref[clear])) <= tol
