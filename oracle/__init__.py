@@ -32,4 +32,5 @@ from .moe_ref import (  # noqa: F401
     topk_softmax,
     widen,
 )
+from .attn_ref import attention_sublayer_ref, gqa_attention_ref, rope_ref  # noqa: F401
 from .params import mistral_param_count, moe_model_param_counts  # noqa: F401

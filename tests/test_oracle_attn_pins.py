@@ -1,0 +1,167 @@
+"""Pins of the attention oracle (GQA with RoPE, "Mixtral" page, "Прямой проход в
+формулах") to facts fixed by mathematics and by independent library routines:
+the complex-number form of the rotation, its relative-position property,
+torch's scaled_dot_product_attention with K/V heads repeated per group,
+causality, and planted mistakes that must fail those pins."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attn_ref
+
+
+def _rng(seed):
+    return np.random.default_rng(1000 + seed)
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def _rope_complex(x, pos, theta):
+    """Pair (2i, 2i+1) as the complex number x_2i + j x_2i+1, times e^{j p theta^(-2i/d_h)}."""
+    x = np.asarray(x, np.float64)
+    dh = x.shape[-1]
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    ang = np.asarray(pos, np.float64)[:, None, None] * theta ** (-2.0 * np.arange(dh // 2) / dh)
+    w = z * np.exp(1j * ang)
+    out = np.empty_like(x)
+    out[..., 0::2], out[..., 1::2] = w.real, w.imag
+    return out
+
+
+@pytest.mark.parametrize("theta", [1e4, 1e6])
+def test_rope_equals_complex_rotation(theta):
+    x = _rng(0).standard_normal((9, 3, 16))
+    pos = np.arange(100, 109)
+    got = attn_ref.rope_ref(x, pos, theta, np.float64)
+    assert np.max(np.abs(got - _rope_complex(x, pos, theta))) < 1e-12
+
+
+def test_rope_position_zero_is_identity_and_norm_is_kept():
+    x = _rng(1).standard_normal((4, 2, 32))
+    assert np.array_equal(attn_ref.rope_ref(x, np.zeros(4), 1e6, np.float64), x)
+    y = attn_ref.rope_ref(x, np.arange(4) * 777, 1e6, np.float64)
+    n = lambda a: np.hypot(a[..., 0::2], a[..., 1::2])
+    assert np.max(np.abs(n(y) - n(x))) < 1e-12
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    q = _rng(2).standard_normal((1, 1, 64))
+    k = _rng(3).standard_normal((1, 1, 64))
+    dot = lambda m, n: float(np.sum(attn_ref.rope_ref(q, [m], 1e6, np.float64) *
+                                    attn_ref.rope_ref(k, [n], 1e6, np.float64)))
+    for shift in (1, 37, 4000):
+        assert abs(dot(10, 3) - dot(10 + shift, 3 + shift)) < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# GQA attention against torch's scaled_dot_product_attention
+# ---------------------------------------------------------------------------
+def _sdpa(q, k, v, causal=True):
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    Q, K, V = t(q).transpose(0, 1), t(k).transpose(0, 1), t(v).transpose(0, 1)  # [heads, T, d_h]
+    r = Q.shape[0] // K.shape[0]
+    K, V = K.repeat_interleave(r, dim=0), V.repeat_interleave(r, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=causal)
+    return o.transpose(0, 1).numpy()
+
+
+@pytest.mark.parametrize("T,H,G,dh", [(17, 8, 2, 16), (33, 4, 4, 8), (20, 6, 1, 32), (1, 4, 2, 16)])
+def test_gqa_matches_torch_sdpa(T, H, G, dh):
+    rng = _rng(T + H)
+    q, k, v = rng.standard_normal((T, H, dh)), rng.standard_normal((T, G, dh)), rng.standard_normal((T, G, dh))
+    got = attn_ref.gqa_attention_ref(q, k, v, True, np.float64)
+    assert np.max(np.abs(got - _sdpa(q, k, v))) < 1e-12
+    got32 = attn_ref.gqa_attention_ref(q, k, v, True)
+    assert np.max(np.abs(got32 - got)) < 1e-5
+
+
+def test_gqa_is_causal():
+    rng = _rng(5)
+    q, k, v = rng.standard_normal((12, 4, 8)), rng.standard_normal((12, 2, 8)), rng.standard_normal((12, 2, 8))
+    a = attn_ref.gqa_attention_ref(q, k, v, True, np.float64)
+    k2, v2 = k.copy(), v.copy()
+    k2[7:] += 3.0
+    v2[7:] -= 5.0
+    b = attn_ref.gqa_attention_ref(q, k2, v2, True, np.float64)
+    assert np.array_equal(a[:7], b[:7]) and not np.allclose(a[7:], b[7:])
+    assert np.allclose(a[0], np.repeat(v[0], 2, axis=0))  # the first query sees only key 0
+
+
+# ---------------------------------------------------------------------------
+# the whole sublayer against a torch composition
+# ---------------------------------------------------------------------------
+def _sublayer_torch(h, gamma, eps, wq, wk, wv, wo, H, G, theta, pos0):
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    F = torch.nn.functional
+    X = F.rms_norm(t(h), (h.shape[1],), t(gamma), eps)
+    T = h.shape[0]
+    dh = wq.shape[0] // H
+    pos = np.arange(pos0, pos0 + T)
+    q = _rope_complex(F.linear(X, t(wq)).reshape(T, H, dh).numpy(), pos, theta)
+    k = _rope_complex(F.linear(X, t(wk)).reshape(T, G, dh).numpy(), pos, theta)
+    v = F.linear(X, t(wv)).reshape(T, G, dh).numpy()
+    o = _sdpa(q, k, v)
+    return (t(h) + F.linear(t(o.reshape(T, H * dh)), t(wo))).numpy()
+
+
+def test_attention_sublayer_matches_torch_composition():
+    rng = _rng(7)
+    T, d, H, G, dh = 21, 64, 8, 2, 16
+    h = rng.standard_normal((T, d)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    wq = (rng.standard_normal((H * dh, d)) / 8).astype(np.float32)
+    wk = (rng.standard_normal((G * dh, d)) / 8).astype(np.float32)
+    wv = (rng.standard_normal((G * dh, d)) / 8).astype(np.float32)
+    wo = (rng.standard_normal((d, H * dh)) / 12).astype(np.float32)
+    ref = _sublayer_torch(h, gamma, 1e-5, wq, wk, wv, wo, H, G, 1e6, 5)
+    got, *_ = attn_ref.attention_sublayer_ref(h, gamma, 1e-5, wq, wk, wv, wo, H, G, 1e6, pos0=5)
+    assert np.max(np.abs(got - ref)) < 1e-4 * np.max(np.abs(ref))
+    got64, *_ = attn_ref.attention_sublayer_ref(h, gamma, 1e-5, wq, wk, wv, wo, H, G, 1e6, pos0=5, dtype=np.float64)
+    assert np.max(np.abs(got64 - ref)) < 1e-12 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes
+# ---------------------------------------------------------------------------
+def _rope_half_split(x, positions, theta, dtype=np.float32):
+    x = np.asarray(x, dtype)
+    dh = x.shape[-1]
+    ang = np.asarray(positions, np.float64)[:, None] * theta ** (-2.0 * np.arange(dh // 2) / dh)
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :dh // 2], x[..., dh // 2:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1).astype(dtype)
+
+
+def _attn_sees_next(q, k, v, causal=True, dtype=np.float32):
+    q, k, v = (np.asarray(a, dtype) for a in (q, k, v))
+    T, H, dh = q.shape
+    r = H // k.shape[1]
+    out = np.empty_like(q)
+    mask = np.where(np.arange(T)[None, :] > np.arange(T)[:, None] + 1, -np.inf, 0.0)
+    for h in range(H):
+        s = q[:, h] @ k[:, h // r].T / np.sqrt(dh) + mask
+        p = np.exp(s - s.max(1, keepdims=True))
+        out[:, h] = (p / p.sum(1, keepdims=True)) @ v[:, h // r]
+    return out
+
+
+def test_planted_rope_pairing_is_caught():
+    x = _rng(8).standard_normal((5, 2, 16))
+    pos = np.arange(3, 8)
+    assert np.max(np.abs(_rope_half_split(x, pos, 1e4, np.float64) - _rope_complex(x, pos, 1e4))) > 1e-2
+
+
+@pytest.mark.parametrize("mutant", ["sees_next", "wrong_group"])
+def test_planted_attention_mistake_is_caught(mutant):
+    rng = _rng(9)
+    q, k, v = rng.standard_normal((10, 8, 8)), rng.standard_normal((10, 2, 8)), rng.standard_normal((10, 2, 8))
+    if mutant == "sees_next":
+        got = _attn_sees_next(q, k, v, True, np.float64)
+    else:
+        G, H = 2, 8
+        kk = np.stack([k[:, h % G] for h in range(H)], axis=1)
+        vv = np.stack([v[:, h % G] for h in range(H)], axis=1)
+        got = attn_ref.gqa_attention_ref(q, kk, vv, True, np.float64)
+    assert np.max(np.abs(got - _sdpa(q, k, v))) > 1e-2
