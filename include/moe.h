@@ -173,6 +173,54 @@ moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float*
                              const moe_expert_bias* expert_bias,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The attention sublayer around the MoE ("Mixtral" page, section "Прямой
+ * проход в формулах": U = H + GQA(RMSNorm_1(H)) with
+ *   Q_h = RoPE(X W_Q^h), K_c = RoPE(X W_K^c), V_c = X W_V^c,
+ *   O_h = softmax(Q_h K_kappa(h)^T / sqrt(d_h) + M) V_kappa(h),
+ *   kappa(h) = h / (H / G), M the causal mask,
+ *   GQA(X) = [O_0; ...; O_{H-1}] W_O).
+ * RoPE turns the pair (2i, 2i+1) of a head vector at position p by the angle
+ * p * rope_theta^(-2i / d_h) (the interleaved form the page's HF loader
+ * implies by permuting q_proj / k_proj rows).  One sequence of T new tokens
+ * at positions pos0 .. pos0 + T - 1, no KV cache, no sliding window.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t T;    /* tokens of the sequence */
+  int32_t d;    /* model width, a positive multiple of 64 */
+  int32_t H;    /* query heads */
+  int32_t G;    /* key / value groups, H % G == 0 */
+  int32_t d_h;  /* head dimension: 128 is implemented */
+  int32_t act;  /* moe_dtype of activations and weights: BF16 is implemented */
+} moe_attn_shape;
+
+/* Bytes of workspace moe_attention_block_forward needs.  0 for an invalid
+ * or unsupported shape.  Host only. */
+size_t moe_attention_workspace_size(const moe_attn_shape* shape);
+
+/* Causal GQA attention core on rotated heads:
+ *   O_h[t] = sum_{s <= t} softmax_s(Q_h[t] . K_kappa(h)[s] / sqrt(d_h)) V_kappa(h)[s]
+ *   q [T][H][d_h], k, v [T][G][d_h], o [T][H][d_h] output, all act (bf16).
+ * Errors as for the MoE calls: MOE_ERR_INVALID_ARG for H % G != 0, odd or
+ * non-positive d_h, NULL / misaligned pointers; MOE_ERR_UNSUPPORTED for
+ * d_h != 128, act != BF16 or T * (H + 2G) * d_h >= 2^31.                     */
+moe_status moe_gqa_attention(const moe_attn_shape* shape, const void* q, const void* k,
+                             const void* v, void* o, void* stream);
+
+/* The whole sublayer, in place: h <- h + GQA(RMSNorm(h) * gamma).
+ *   h_inout  [T][d] act
+ *   gamma    [d] fp32;  eps > 0
+ *   wqkv     [(H + 2G) d_h][d] act: the rows of W_Q ([H d_h][d]), then W_K,
+ *            then W_V ([G d_h][d] each), nn.Linear layout (the pages' three
+ *            Linear weights stacked row-wise)
+ *   wo       [d][H d_h] act
+ *   rope_theta > 0 (Mixtral 8x7B: 1e6);  pos0 >= 0
+ *   ws >= moe_attention_workspace_size(shape) bytes                          */
+moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inout,
+                                       const float* gamma, float eps, const void* wqkv,
+                                       const void* wo, float rope_theta, int64_t pos0,
+                                       void* ws, size_t ws_bytes, void* stream);
+
 /* Router load-balancing loss ("Mixtral" page, section "Load-balancing
  * loss"): L_aux = alpha * E * sum_{s<k} sum_i f_{s,i} * P_i, where f_{s,i} is
  * the share of tokens whose s-th largest logit is expert i (ties -> lower

@@ -27,6 +27,17 @@ class MoEShape(ctypes.Structure):
     ]
 
 
+class MoEAttnShape(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("d", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("G", ctypes.c_int32),
+        ("d_h", ctypes.c_int32),
+        ("act", ctypes.c_int32),
+    ]
+
+
 class MoEExpertBias(ctypes.Structure):
     _fields_ = [("b1", ctypes.c_void_p), ("b3", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
 
@@ -34,6 +45,7 @@ class MoEExpertBias(ctypes.Structure):
 _vp = ctypes.c_void_p
 _sp = ctypes.POINTER(MoEShape)
 _bp = ctypes.POINTER(MoEExpertBias)
+_ap = ctypes.POINTER(MoEAttnShape)
 
 # name -> (restype, argtypes)
 SIGNATURES = {
@@ -47,6 +59,10 @@ SIGNATURES = {
     "moe_block_forward": (ctypes.c_int, [_sp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _bp, _vp,
                                          ctypes.c_size_t, _vp]),
     "moe_aux_loss": (ctypes.c_int, [_sp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp]),
+    "moe_attention_workspace_size": (ctypes.c_size_t, [_ap]),
+    "moe_gqa_attention": (ctypes.c_int, [_ap, _vp, _vp, _vp, _vp, _vp]),
+    "moe_attention_block_forward": (ctypes.c_int, [_ap, _vp, _vp, ctypes.c_float, _vp, _vp, ctypes.c_float,
+                                                   ctypes.c_int64, _vp, ctypes.c_size_t, _vp]),
     "moe_set_timing_events": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_gemm.hip", "expert_stream.hip", "combine.hip", "aux_loss.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_ffn.hip", "expert_gemm.hip", "expert_stream.hip", "combine.hip", "aux_loss.hip", "attention.hip", "moe_api.cpp"]
 
 # Packed fp32 instructions are disabled for every HIP translation unit.
 HIP_FLAGS = [

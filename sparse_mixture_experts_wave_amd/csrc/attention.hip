@@ -1,0 +1,327 @@
+// The attention sublayer around the MoE ("Mixtral" textbook page, section
+// "Прямой проход в формулах": U = H + GQA(RMSNorm_1(H)), with
+// Q_h = RoPE(X W_Q^h), K_c = RoPE(X W_K^c), V_c = X W_V^c,
+// O_h = softmax(Q_h K_kappa(h)^T / sqrt(d_h) + M) V_kappa(h), kappa(h) = h / (H/G),
+// M the causal mask, GQA(X) = [O_0; ...; O_{H-1}] W_O).
+//
+// Kernels here: a row RMSNorm, the RoPE rotation that also splits the fused
+// Q|K|V projection into bf16 head-major tensors, the causal GQA flash
+// attention, and the residual add after W_O.  The two projections run on the
+// grouped MFMA GEMM of the experts (one "expert", no gather).
+//
+// RoPE reading: the page defers the rotation to another chapter; its
+// HuggingFace loader permutes the rows of q_proj / k_proj per head, which
+// turns HF's half-split rotation into the interleaved one.  So pair
+// (2i, 2i+1) of a head vector at position p turns by p * theta^(-2i/d_h).
+//
+// Flash attention.  A 256-thread workgroup owns 128 queries of one head (32
+// per wave) and walks the key axis in 64-key tiles up to the diagonal.  Each
+// wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that a lane's
+// accumulator column is one query: the running max, the exponentials and the
+// running sum of a query stay in its lane and the lane 32 apart (one
+// cross-lane exchange per tile).  P^T then feeds O^T = V^T P^T straight from
+// registers as the B operand: the k-index order of the MFMA is taken to be the
+// order in which the S^T accumulator holds the keys, and V^T is read from LDS
+// in that same order.  K is staged in LDS as [key][d_h] with 16-byte chunks
+// XOR-swizzled by key; V is staged transposed, [d_h][key], in 136-byte rows so
+// the 32 head dimensions an operand read touches fall in distinct banks.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// RMSNorm of rows: u = x / sqrt(mean x^2 + eps) * gamma, rounded to bf16
+// ---------------------------------------------------------------------------
+constexpr int RN_T = 256;
+
+__global__ __launch_bounds__(RN_T) void rmsnorm_rows_kernel(const uint16_t* __restrict__ x,
+                                                            const float* __restrict__ gamma, float eps,
+                                                            uint16_t* __restrict__ u, int d) {
+  __shared__ float part[RN_T / kWave];
+  const uint16_t* xr = x + static_cast<int64_t>(blockIdx.x) * d;
+  uint16_t* ur = u + static_cast<int64_t>(blockIdx.x) * d;
+  float ss = 0.f;
+  for (int j = threadIdx.x * 8; j < d; j += RN_T * 8) {
+    const u32x4 w = load16(xr + j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = lo_bf16(w[i]), b = hi_bf16(w[i]);
+      ss += a * a + b * b;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < RN_T / kWave; ++w) tot += part[w];
+  const float rinv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+  for (int j = threadIdx.x * 8; j < d; j += RN_T * 8) {
+    const u32x4 w = load16(xr + j);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = pack_bf16x2(lo_bf16(w[i]) * rinv * gamma[j + 2 * i], hi_bf16(w[i]) * rinv * gamma[j + 2 * i + 1]);
+    store16(ur + j, o);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RoPE + split: qkv fp32 [T][(H + 2G) d_h] -> q [T][H][d_h], k, v [T][G][d_h] bf16
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rope_pack_kernel(const float* __restrict__ qkv, uint16_t* __restrict__ q,
+                                                        uint16_t* __restrict__ k, uint16_t* __restrict__ v,
+                                                        int64_t T, int H, int G, int dh, double theta,
+                                                        int64_t pos0) {
+  const int half = dh / 2;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= T * half) return;
+  const int64_t t = idx / half;
+  const int i = static_cast<int>(idx - t * half);
+  // The angle in fp64: positions reach 10^4 .. 10^5 and an fp32 angle would be
+  // off by up to ~1e-2 rad there.
+  const double ang = static_cast<double>(pos0 + t) * pow(theta, -2.0 * i / dh);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  const float c = static_cast<float>(cd), s = static_cast<float>(sd);
+  const float* row = qkv + t * static_cast<int64_t>(H + 2 * G) * dh + 2 * i;
+  for (int hh = 0; hh < H + G; ++hh) {
+    const float2 x = *reinterpret_cast<const float2*>(row + static_cast<int64_t>(hh) * dh);
+    const uint32_t r = pack_bf16x2(x.x * c - x.y * s, x.x * s + x.y * c);
+    uint16_t* dst = hh < H ? q + (t * H + hh) * dh : k + (t * G + (hh - H)) * dh;
+    *reinterpret_cast<uint32_t*>(dst + 2 * i) = r;
+  }
+  for (int gg = 0; gg < G; ++gg) {
+    const float2 x = *reinterpret_cast<const float2*>(row + static_cast<int64_t>(H + G + gg) * dh);
+    *reinterpret_cast<uint32_t*>(v + (t * G + gg) * dh + 2 * i) = pack_bf16x2(x.x, x.y);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual: h += y (fp32), one rounding to bf16
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void residual_add_kernel(uint16_t* __restrict__ h, const float* __restrict__ y,
+                                                           int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 w = load16(h + 8 * i);
+  const float4 a = *reinterpret_cast<const float4*>(y + 8 * i);
+  const float4 b = *reinterpret_cast<const float4*>(y + 8 * i + 4);
+  u32x4 o;
+  o[0] = pack_bf16x2(lo_bf16(w[0]) + a.x, hi_bf16(w[0]) + a.y);
+  o[1] = pack_bf16x2(lo_bf16(w[1]) + a.z, hi_bf16(w[1]) + a.w);
+  o[2] = pack_bf16x2(lo_bf16(w[2]) + b.x, hi_bf16(w[2]) + b.y);
+  o[3] = pack_bf16x2(lo_bf16(w[3]) + b.z, hi_bf16(w[3]) + b.w);
+  store16(h + 8 * i, o);
+}
+
+__global__ void row_range_kernel(int32_t* __restrict__ offsets, int32_t rows) {
+  if (threadIdx.x == 0) {
+    offsets[0] = 0;
+    offsets[1] = rows;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// causal GQA flash attention, d_h = 128
+// ---------------------------------------------------------------------------
+constexpr int FA_D = 128;                // head dimension
+constexpr int FA_BQ = 128;               // queries per workgroup (4 waves x 32)
+constexpr int FA_BKV = 64;               // keys per tile
+constexpr int FA_NT = 256;
+constexpr int VT_STRIDE = FA_BKV + 4;    // 68 bf16 = 136 bytes per transposed V row
+
+__device__ __forceinline__ int kswz(int key, int chunk) { return key * FA_D + ((chunk ^ (key & 15)) << 3); }
+
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+
+__global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ o, int T, int H, int G,
+                                                               float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[FA_BKV * FA_D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[FA_D * VT_STRIDE];
+
+  const int h = blockIdx.x;                                   // heads of a K/V group are adjacent
+  const int n_qt = (T + FA_BQ - 1) / FA_BQ;
+  const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * FA_BQ;  // longest rows first
+  const int g = h / (H / G);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int qw = q0 + wave * 32;         // first query of the wave
+  const int my_q = qw + (lane & 31);     // the lane's query: its column of S^T and O^T
+  const int64_t ld_q = static_cast<int64_t>(H) * FA_D;
+  const int64_t ld_kv = static_cast<int64_t>(G) * FA_D;
+
+  // B operand of S^T = K Q^T: lane holds query my_q, dims 16 ks + 8 half .. +7.
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = q + static_cast<int64_t>(min(my_q, T - 1)) * ld_q + h * FA_D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(load16(qp + 16 * ks));
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = min(T, q0 + FA_BQ);
+  for (int kv0 = 0; kv0 < kv_end; kv0 += FA_BKV) {
+    // K tile: row = key, 16 swizzled chunks of 16 bytes.  Keys past T are
+    // clamped to T-1; they lie above every query, so the mask removes them.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid * 4 + i;
+      const int key = c >> 4, chunk = c & 15;
+      const int kk = min(kv0 + key, T - 1);
+      store16(Ks + kswz(key, chunk), load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + chunk * 8));
+    }
+    // V tile, transposed: thread holds keys 4 kg .. 4 kg + 3, dims 8 dg .. 8 dg + 7.
+    {
+      const int kg = tid & 15, dg = tid >> 4;
+      u32x4 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = load16(v + static_cast<int64_t>(min(kv0 + 4 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = (j & 1) ? hi16(r[i][j >> 1]) : lo16(r[i][j >> 1]);
+        uint2 packed;
+        packed.x = e[0] | (e[1] << 16);
+        packed.y = e[2] | (e[3] << 16);
+        *reinterpret_cast<uint2*>(Vt + (8 * dg + j) * VT_STRIDE + 4 * kg) = packed;
+      }
+    }
+    __syncthreads();
+
+    if (kv0 <= qw + 31) {  // some key of the tile is visible to some query of the wave
+      // S^T: rows = keys kv0 + 32 kb + 8 (e / 4) + 4 half + e % 4, column = my_q.
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 a = as_bf16x8(load16(Ks + kswz(kb * 32 + (lane & 31), 2 * ks + half)));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+          const float x = key > my_q ? -INFINITY : s[kb][e] * scale_log2;
+          s[kb][e] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m, mt);  // finite: key kv0 = 0 is visible to every query
+      const float alpha = exp2f(m - m_new);
+      float lt = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(s[kb][e] - m_new);
+          s[kb][e] = p;
+          lt += p;
+        }
+      lt += __shfl_xor(lt, 32);
+      l = l * alpha + lt;
+      m = m_new;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      // O^T += V^T P^T over four 16-key steps.  Step j takes accumulator
+      // entries e = 8 (j & 1) .. +7 of block j >> 1: for lane half q these are
+      // keys base + 0..3 and base + 8..11 with base = 32 (j>>1) + 16 (j&1) + 4q,
+      // and the A operand reads V^T at exactly those keys.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = j >> 1, hf = j & 1;
+        u32x4 pw;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * hf + 2 * t], s[kb][8 * hf + 2 * t + 1]);
+        const bf16x8 pb = as_bf16x8(pw);
+        const int base = kb * 32 + hf * 16 + 4 * half;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint16_t* vr = Vt + (db * 32 + (lane & 31)) * VT_STRIDE + base;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+          u32x4 aw;
+          aw[0] = lo.x;
+          aw[1] = lo.y;
+          aw[2] = hi.x;
+          aw[3] = hi.y;
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aw), pb, oacc[db], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4.
+  if (my_q < T) {
+    const float inv = 1.0f / l;
+    uint16_t* op = o + static_cast<int64_t>(my_q) * ld_q + h * FA_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) op[db * 32 + 8 * (e >> 2) + 4 * half + (e & 3)] = f32_to_bf16(oacc[db][e] * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
+                               hipStream_t stream) {
+  rmsnorm_rows_kernel<<<static_cast<unsigned>(T), RN_T, 0, stream>>>(x, gamma, eps, u, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_pack(const float* qkv, uint16_t* q, uint16_t* k, uint16_t* v, int64_t T, int H, int G,
+                            int dh, double theta, int64_t pos0, hipStream_t stream) {
+  const int64_t n = T * (dh / 2);
+  rope_pack_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(qkv, q, k, v, T, H, G, dh, theta,
+                                                                               pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_add(uint16_t* h, const float* y, int64_t n, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  residual_add_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(h, y, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_range(int32_t* offsets, int64_t rows, hipStream_t stream) {
+  row_range_kernel<<<1, 64, 0, stream>>>(offsets, static_cast<int32_t>(rows));
+  return hipGetLastError();
+}
+
+bool flash_attn_supported(int dh) { return dh == FA_D; }
+
+hipError_t launch_flash_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
+                             int H, int G, int dh, hipStream_t stream) {
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(dh)));
+  const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + FA_BQ - 1) / FA_BQ));
+  flash_attn_fwd_kernel<<<grid, FA_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace moe

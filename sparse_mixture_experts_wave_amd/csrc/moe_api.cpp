@@ -1,9 +1,11 @@
 // C ABI of the MoE layer: argument validation, workspace carving and the
-// launch sequence route -> dispatch -> experts -> combine.  Host code only;
+// launch sequence route -> dispatch -> experts -> combine (and, for the
+// attention sublayer, rmsnorm -> qkv -> rope -> attention -> output -> residual).  Host code only;
 // every launch is asynchronous on the caller's stream and nothing here
 // synchronises or reads device memory.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -210,6 +212,48 @@ moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, 
   return mark(5, stream);
 }
 
+// ---------------------------------------------------------------------------
+// attention sublayer
+// ---------------------------------------------------------------------------
+moe_status check_attn_shape(const moe_attn_shape* s) {
+  if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(s->T));
+  if (s->d <= 0 || s->d % 64 != 0 || s->d > 32768)
+    return fail(MOE_ERR_INVALID_ARG, "d = %d must be a positive multiple of 64, at most 32768", s->d);
+  if (s->H < 1 || s->G < 1 || s->H % s->G != 0 || s->H > 1024)
+    return fail(MOE_ERR_INVALID_ARG, "H = %d, G = %d: need 1 <= G, H %% G == 0, H <= 1024", s->H, s->G);
+  if (s->d_h <= 0 || s->d_h % 2 != 0) return fail(MOE_ERR_INVALID_ARG, "d_h = %d must be positive and even", s->d_h);
+  if (s->act != MOE_F32 && s->act != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "act dtype %d unknown", s->act);
+  if (!moe::flash_attn_supported(s->d_h)) return fail(MOE_ERR_UNSUPPORTED, "d_h = %d: only 128 is implemented", s->d_h);
+  if (s->act != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "attention is implemented for bf16 only");
+  const int64_t widest = std::max<int64_t>(s->d, static_cast<int64_t>(s->H + 2 * s->G) * s->d_h);
+  if (s->T * widest >= (int64_t{1} << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * %lld = %lld: at most 2^31 - 1 elements per activation tensor",
+                static_cast<long long>(widest), static_cast<long long>(s->T * widest));
+  return MOE_OK;
+}
+
+struct AttnLayout {
+  size_t offsets, xn, qkv, q, k, v, o, oproj, total;
+};
+
+AttnLayout attn_layout(const moe_attn_shape* s) {
+  const size_t T = static_cast<size_t>(s->T);
+  const size_t nq = static_cast<size_t>(s->H) * s->d_h, nkv = static_cast<size_t>(s->G) * s->d_h;
+  AttnLayout L{};
+  size_t at = 0;
+  L.offsets = at; at += up(2 * 4);
+  L.xn = at; at += up(T * s->d * 2);
+  L.qkv = at; at += up(T * (nq + 2 * nkv) * 4);
+  L.q = at; at += up(T * nq * 2);
+  L.k = at; at += up(T * nkv * 2);
+  L.v = at; at += up(T * nkv * 2);
+  L.o = at; at += up(T * nq * 2);
+  L.oproj = at; at += up(T * s->d * 4);
+  L.total = at;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +394,70 @@ moe_status moe_aux_loss(const moe_shape* shape, const float* logits, int32_t num
   return hip_status(moe::launch_aux_loss(logits, num_layers, shape->T, shape->E, shape->k, token_mask, alpha, loss,
                                          stats, hs(stream)),
                     "aux loss launch");
+}
+
+size_t moe_attention_workspace_size(const moe_attn_shape* shape) {
+  if (check_attn_shape(shape) != MOE_OK) return 0;
+  return attn_layout(shape).total;
+}
+
+moe_status moe_gqa_attention(const moe_attn_shape* shape, const void* q, const void* k, const void* v, void* o,
+                             void* stream) {
+  MOE_TRY(check_attn_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(q, "q"));
+  MOE_TRY(need(k, "k"));
+  MOE_TRY(need(v, "v"));
+  MOE_TRY(need(o, "o"));
+  return hip_status(moe::launch_flash_attn(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), shape->T,
+                                           shape->H, shape->G, shape->d_h, hs(stream)),
+                    "attention launch");
+}
+
+moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inout, const float* gamma, float eps,
+                                       const void* wqkv, const void* wo, float rope_theta, int64_t pos0, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  MOE_TRY(check_attn_shape(shape));
+  if (!(eps > 0.f)) return fail(MOE_ERR_INVALID_ARG, "eps = %g must be > 0", static_cast<double>(eps));
+  if (!(rope_theta > 0.f))
+    return fail(MOE_ERR_INVALID_ARG, "rope_theta = %g must be > 0", static_cast<double>(rope_theta));
+  if (pos0 < 0 || pos0 > (int64_t{1} << 40))
+    return fail(MOE_ERR_INVALID_ARG, "pos0 = %lld out of range", static_cast<long long>(pos0));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(h_inout, "h_inout"));
+  MOE_TRY(need(gamma, "gamma"));
+  MOE_TRY(need(wqkv, "wqkv"));
+  MOE_TRY(need(wo, "wo"));
+  MOE_TRY(need(ws, "ws"));
+  const AttnLayout L = attn_layout(shape);
+  if (ws_bytes < L.total) return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
+  const int64_t T = shape->T;
+  const int d = shape->d, H = shape->H, G = shape->G, dh = shape->d_h;
+  const int nqkv = (H + 2 * G) * dh, nq = H * dh;
+  int32_t* off = at<int32_t>(ws, L.offsets);
+  uint16_t* xn = at<uint16_t>(ws, L.xn);
+  float* qkv = at<float>(ws, L.qkv);
+  uint16_t* q = at<uint16_t>(ws, L.q);
+  uint16_t* k = at<uint16_t>(ws, L.k);
+  uint16_t* v = at<uint16_t>(ws, L.v);
+  uint16_t* o = at<uint16_t>(ws, L.o);
+  float* oproj = at<float>(ws, L.oproj);
+  uint16_t* h = static_cast<uint16_t*>(h_inout);
+  const hipStream_t st = hs(stream);
+  // The projections run on the experts' GEMM as a single expert owning all T rows.
+  MOE_TRY(hip_status(moe::launch_row_range(off, T, st), "row range launch"));
+  MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st), "rmsnorm launch"));
+  MOE_TRY(hip_status(moe::launch_expert_down_bf16(xn, off, static_cast<const uint16_t*>(wqkv), nullptr, qkv, T, 1,
+                                                  nqkv, d, 1, st),
+                     "qkv projection launch"));
+  MOE_TRY(hip_status(moe::launch_rope_pack(qkv, q, k, v, T, H, G, dh, static_cast<double>(rope_theta), pos0, st),
+                     "rope launch"));
+  MOE_TRY(hip_status(moe::launch_flash_attn(q, k, v, o, T, H, G, dh, st), "attention launch"));
+  MOE_TRY(hip_status(moe::launch_expert_down_bf16(o, off, static_cast<const uint16_t*>(wo), nullptr, oproj, T, 1, d,
+                                                  nq, 1, st),
+                     "output projection launch"));
+  return hip_status(moe::launch_residual_add(h, oproj, T * d, st), "residual launch");
 }
 
 moe_status moe_set_timing_events(void* const* events, int32_t count) {

@@ -211,3 +211,49 @@ def moe_aux_loss(logits: torch.Tensor, k: int = 2, alpha: float = 1.0,
     _lib.check(_lib.load().moe_aux_loss(ctypes.byref(shape), _p(logits), int(L), _p(token_mask), float(alpha),
                                         _p(loss), _p(stats), _stream(logits)))
     return loss, stats
+
+
+# ---------------------------------------------------------------------------
+# the attention sublayer around the MoE
+# ---------------------------------------------------------------------------
+def make_attn_shape(T: int, d: int, H: int, G: int, d_h: int, act: torch.dtype = torch.bfloat16) -> _lib.MoEAttnShape:
+    return _lib.MoEAttnShape(int(T), int(d), int(H), int(G), int(d_h), _DT.get(act, -1))
+
+
+def attention_workspace_size(shape: _lib.MoEAttnShape) -> int:
+    return int(_lib.load().moe_attention_workspace_size(ctypes.byref(shape)))
+
+
+def moe_gqa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal GQA attention on rotated heads: q [T, H, d_h], k, v [T, G, d_h] -> o [T, H, d_h]."""
+    q, k, v = _gpu(q, "q"), _gpu(k, "k"), _gpu(v, "v")
+    T, H, dh = q.shape
+    G = k.shape[1]
+    if tuple(k.shape) != (T, G, dh) or tuple(v.shape) != (T, G, dh):
+        raise ValueError("k and v must be [T, G, d_h] with q [T, H, d_h]")
+    shape = make_attn_shape(T, d if d is not None else H * dh, H, G, dh, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    _lib.check(_lib.load().moe_gqa_attention(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(out), _stream(q)))
+    return out
+
+
+def moe_attention_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, wqkv: torch.Tensor,
+                                wo: torch.Tensor, H: int, G: int, rope_theta: float = 1e6, pos0: int = 0,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """In place: h <- h + GQA(RMSNorm(h) * gamma) with RoPE (causal, positions pos0 ..).
+
+    wqkv is [(H + 2G) d_h, d]: W_Q rows, then W_K, then W_V; wo is [d, H d_h]."""
+    h, gamma, wqkv, wo = _gpu(h, "h"), _gpu(gamma, "gamma"), _gpu(wqkv, "wqkv"), _gpu(wo, "wo")
+    T, d = h.shape
+    dh = wo.shape[1] // H
+    if tuple(wqkv.shape) != ((H + 2 * G) * dh, d) or tuple(wo.shape) != (d, H * dh):
+        raise ValueError("wqkv must be [(H + 2G) d_h, d] and wo [d, H d_h]")
+    shape = make_attn_shape(T, d, H, G, dh, h.dtype)
+    if workspace is None:
+        workspace = _ws(attention_workspace_size(shape), h.device)
+    _lib.check(_lib.load().moe_attention_block_forward(ctypes.byref(shape), _p(h), _p(gamma), float(eps), _p(wqkv),
+                                                       _p(wo), float(rope_theta), int(pos0), _p(workspace),
+                                                       workspace.numel(), _stream(h)))
+    return h

@@ -198,3 +198,36 @@ def generate_torch(cfg: MoEConfig, device, layer: int = 0, seed: int = 0):
         "w2": stack(cfg.d, cfg.d_ff, cfg.w2_std, "w2"),
     }
     return res
+
+
+# ---------------------------------------------------------------------------
+# inputs of the attention sublayer around the MoE (GQA with RoPE)
+# ---------------------------------------------------------------------------
+ATTN_TENSOR_IDS = {"h": 20, "wqkv": 21, "wo": 22, "q": 23, "k": 24, "v": 25, "gamma": 26}
+
+
+def _attn_rng(seed: int, cfg_id: int, tensor: str) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(cfg_id, 0, ATTN_TENSOR_IDS[tensor])))
+
+
+def attention_inputs(T: int, d: int, H: int, G: int, dh: int, cfg_id: int = 40, seed: int = 0,
+                     gamma: str = "ones") -> Dict[str, np.ndarray]:
+    """One sublayer's inputs, bf16 bits: h [T, d] ~ N(0, 1); wqkv [(H + 2G) dh, d] and
+    wo [d, H dh] with variance 1/fan_in (rows of W_Q, then W_K, then W_V); gamma fp32
+    ones (the pages' initial value) or uniform(0.5, 1.5) with gamma="random"."""
+    out = {
+        "h": bf16_bits_from_f32(_normal(_attn_rng(seed, cfg_id, "h"), (T, d), 1.0)),
+        "wqkv": bf16_bits_from_f32(_normal(_attn_rng(seed, cfg_id, "wqkv"), ((H + 2 * G) * dh, d), 1 / math.sqrt(d))),
+        "wo": bf16_bits_from_f32(_normal(_attn_rng(seed, cfg_id, "wo"), (d, H * dh), 1 / math.sqrt(H * dh))),
+    }
+    if gamma == "ones":
+        out["gamma"] = np.ones(d, np.float32)
+    else:
+        out["gamma"] = _attn_rng(seed, cfg_id, "gamma").uniform(0.5, 1.5, d).astype(np.float32)
+    return out
+
+
+def attention_heads(T: int, H: int, G: int, dh: int, cfg_id: int = 41, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Rotated-head inputs of the attention core, bf16 bits: q [T, H, dh], k, v [T, G, dh] ~ N(0, 1)."""
+    return {n: bf16_bits_from_f32(_normal(_attn_rng(seed, cfg_id, n), (T, H if n == "q" else G, dh), 1.0))
+            for n in ("q", "k", "v")}

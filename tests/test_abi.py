@@ -30,7 +30,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = _declared()
     assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward",
-            "moe_block_forward", "moe_workspace_size", "moe_last_error"} <= set(names)
+            "moe_block_forward", "moe_workspace_size", "moe_last_error", "moe_attention_workspace_size",
+            "moe_gqa_attention", "moe_attention_block_forward"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -138,3 +139,51 @@ def test_python_binding_maps_status_to_exceptions(lib):
     with pytest.raises(NotImplementedError):
         _lib.check(route(lib, shape(E=16, k=9)))
     _lib.check(_lib.MOE_OK)
+
+
+# ---------------------------------------------------------------------------
+# attention sublayer entry points (validation only: no GPU here)
+# ---------------------------------------------------------------------------
+def attn_shape(T=128, d=4096, H=32, G=8, d_h=128, act=_lib.MOE_BF16):
+    return _lib.MoEAttnShape(T, d, H, G, d_h, act)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d=100), _lib.MOE_ERR_INVALID_ARG),
+    (dict(H=32, G=6), _lib.MOE_ERR_INVALID_ARG),
+    (dict(G=0), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d_h=127), _lib.MOE_ERR_INVALID_ARG),
+    (dict(d_h=64), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(act=_lib.MOE_F32), _lib.MOE_ERR_UNSUPPORTED),
+    (dict(act=9), _lib.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 19), _lib.MOE_ERR_UNSUPPORTED),  # T * (H + 2G) * d_h >= 2^31
+])
+def test_attention_shape_validation(lib, kw, status):
+    s = attn_shape(**kw)
+    assert lib.moe_gqa_attention(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_attention_workspace_size(ctypes.byref(s)) == 0
+
+
+def test_attention_block_validation(lib):
+    s = attn_shape()
+    call = lambda **kw: lib.moe_attention_block_forward(
+        ctypes.byref(s), kw.get("h", FAKE), FAKE, kw.get("eps", 1e-5), FAKE, FAKE, kw.get("theta", 1e6),
+        kw.get("pos0", 0), FAKE, kw.get("ws_bytes", 1 << 40), None)
+    assert call(eps=0.0) == _lib.MOE_ERR_INVALID_ARG and b"eps" in lib.moe_last_error()
+    assert call(theta=0.0) == _lib.MOE_ERR_INVALID_ARG and b"rope_theta" in lib.moe_last_error()
+    assert call(pos0=-1) == _lib.MOE_ERR_INVALID_ARG
+    assert call(h=None) == _lib.MOE_ERR_INVALID_ARG and b"h_inout" in lib.moe_last_error()
+    assert call(h=MISALIGNED) == _lib.MOE_ERR_INVALID_ARG
+    assert call(ws_bytes=1024) == _lib.MOE_ERR_INVALID_ARG and b"workspace" in lib.moe_last_error()
+    s0 = attn_shape(T=0)
+    assert lib.moe_attention_block_forward(ctypes.byref(s0), FAKE, FAKE, 1e-5, FAKE, FAKE, 1e6, 0, None, 0,
+                                           None) == _lib.MOE_OK
+    assert lib.moe_gqa_attention(ctypes.byref(s0), None, None, None, None, None) == _lib.MOE_OK
+
+
+def test_attention_workspace_size(lib):
+    T, d, H, G, dh = 4096, 4096, 32, 8, 128
+    ws = lib.moe_attention_workspace_size(ctypes.byref(attn_shape(T=T, d=d, H=H, G=G, d_h=dh)))
+    need = T * d * 2 + T * (H + 2 * G) * dh * 4 + T * H * dh * 2 * 2 + T * G * dh * 2 * 2 + T * d * 4
+    assert need <= ws < need + (1 << 20)
