@@ -11,7 +11,9 @@ already resident in HBM.  Prints one JSON line.
 The default workload is the Mixtral 8x7B layer in the decode regime (T = 16,
 HBM-bound); the prefill layer (T = 4096), the Zipf-skewed layer (T = 16384)
 and the 32-layer residual stack (T = 2048, one step = all 32 sublayers) are
-measured too and reported under "secondary".  Per-kernel durations come from HIP events that
+measured too and reported under "secondary"; the small-T decode latency
+sweep under "decode_latency"; the attention sublayer around the MoE (GQA with
+RoPE at Mixtral widths, T = 4096) and a whole decoder layer under "attention".  Per-kernel durations come from HIP events that
 moe_forward records on its own stream between its kernels (timing points of
 the C ABI); the roofline fraction is that of the dominant kernel.
 """
@@ -302,6 +304,78 @@ def measure_decode_latency(steps: int, Ts=(1, 2, 4, 8, 16)):
     return out
 
 
+def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: int = 8, dh: int = 128,
+                      theta: float = 1e6):
+    """The attention sublayer around the MoE at Mixtral 8x7B widths (32 query
+    heads, 8 K/V groups, d_h = 128, rope_theta 1e6), one causal sequence of T
+    tokens: the causal GQA core alone (moe_gqa_attention) and the whole
+    sublayer h <- h + GQA(RMSNorm(h)) (moe_attention_block_forward), plus a
+    full decoder layer = that sublayer followed by the MoE sublayer
+    (moe_block_forward on the prefill workload's weights)."""
+    import torch
+
+    import sparse_mixture_experts_wave_amd as moe
+    from synth import CONFIGS, attention_heads, attention_inputs, generate_torch
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)
+
+    inp = attention_inputs(T, d, H, G, dh)
+    heads = attention_heads(T, H, G, dh)
+    h0 = bf16(inp["h"])
+    gamma = torch.from_numpy(inp["gamma"]).to(dev)
+    wqkv, wo = bf16(inp["wqkv"]), bf16(inp["wo"])
+    q, k, v = bf16(heads["q"]), bf16(heads["k"]), bf16(heads["v"])
+    o = torch.empty_like(q)
+    shape = moe.make_attn_shape(T, d, H, G, dh)
+    ws = torch.empty(moe.attention_workspace_size(shape), dtype=torch.uint8, device=dev)
+    h = h0.clone()
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    core_ms = timed(lambda: moe.moe_gqa_attention(q, k, v, out=o), steps)
+    sub_ms = timed(lambda: moe.moe_attention_block_forward(h, gamma, 1e-5, wqkv, wo, H, G, theta, 0, ws), steps)
+
+    cfg = CONFIGS["mixtral_prefill_t4096"].with_(T=T)
+    mw = generate_torch(cfg, dev)
+    mshape = moe.make_shape(T, cfg.d, cfg.d_ff, cfg.E, cfg.k, torch.bfloat16)
+    mws = torch.empty(moe.workspace_size(mshape), dtype=torch.uint8, device=dev)
+    ones = torch.ones(cfg.d, dtype=torch.float32, device=dev)
+
+    def layer():
+        moe.moe_attention_block_forward(h, gamma, 1e-5, wqkv, wo, H, G, theta, 0, ws)
+        moe.moe_block_forward(h, ones, 1e-5, mw["w_gate"], mw["bias"], mw["w1"], mw["w3"], mw["w2"],
+                              workspace=mws)
+
+    h.copy_(h0)
+    layer_ms = timed(layer, max(3, steps // 2))
+    core_flops = 2.0 * 2 * dh * H * T * (T + 1) / 2       # Q K^T and P V over the causal triangle
+    proj_flops = 2.0 * T * d * (H + 2 * G) * dh + 2.0 * T * H * dh * d
+    moe_flops = 6.0 * cfg.k * T * cfg.d * cfg.d_ff
+    core_tf = core_flops / (core_ms * 1e-3) / 1e12
+    return {
+        "workload": f"mixtral_attention_t{T}", "T": T, "d": d, "H": H, "G": G, "d_h": dh, "rope_theta": theta,
+        "core_ms": round(core_ms, 4), "sublayer_ms": round(sub_ms, 4),
+        "sublayer_tokens_per_s": round(T / (sub_ms * 1e-3), 1),
+        "sublayer_tflops": round((core_flops + proj_flops) / (sub_ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": "flash_attn", "achieved": round(core_tf, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(core_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms": round(core_ms, 4)},
+        "decoder_layer": {"ms": round(layer_ms, 4), "tokens_per_s": round(T / (layer_ms * 1e-3), 1),
+                          "tflops": round((core_flops + proj_flops + moe_flops) / (layer_ms * 1e-3) / 1e12, 2)},
+    }
+
+
 def roofline(res):
     cfg, work, pk = res["cfg"], res["work"], res["per_kernel_ms"]
     dom = max(("expert_up", "expert_down"), key=lambda n: pk[n])
@@ -382,6 +456,7 @@ def main():
                     help="comma-separated workloads also measured and reported under 'secondary', or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true", help="skip the small-T decode latency sweep")
+    ap.add_argument("--no-attention", action="store_true", help="skip the attention sublayer workload")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json for --config from rocprofv3 --pmc CSVs (no GPU needed)")
@@ -432,6 +507,11 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] decode latency sweep", file=sys.stderr, flush=True)
         latency = measure_decode_latency(a.steps)
+    attention = None
+    if not a.no_attention:
+        torch.cuda.empty_cache()
+        print("[bench] attention sublayer", file=sys.stderr, flush=True)
+        attention = measure_attention(max(3, a.steps // 2))
     out = {
         "metric": METRIC, "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -439,7 +519,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "k": cfg.k,
                    "parallelism": "single GPU"},
         "roofline": prim["roofline"], "cpu_baseline": cpu, "detail": prim, "secondary": sec,
-        "decode_latency": latency,
+        "decode_latency": latency, "attention": attention,
     }
     print(json.dumps(out), flush=True)
 
