@@ -137,9 +137,17 @@ constexpr int VT_STRIDE = FA_BKV + 4;    // 68 bf16 = 136 bytes per transposed V
 __device__ __forceinline__ int kswz(int key, int chunk) { return key * FA_D + ((chunk ^ (key & 15)) << 3); }
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
-__global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
                                                                uint16_t* __restrict__ o, int T, int H, int G,
@@ -175,35 +183,45 @@ __global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* _
   float m = -INFINITY, l = 0.f;
 
   const int kv_end = min(T, q0 + FA_BQ);
-  for (int kv0 = 0; kv0 < kv_end; kv0 += FA_BKV) {
-    // K tile: row = key, 16 swizzled chunks of 16 bytes.  Keys past T are
-    // clamped to T-1; they lie above every query, so the mask removes them.
+  // Tile t+1 is loaded into registers while tile t is computed from LDS, and
+  // stored to LDS between two barriers once every wave is done with tile t.
+  // K: 4 x 16-byte chunks of rows key = c / 16 (c = 4 tid + i); V: keys
+  // 4 kg .. 4 kg + 3 x dims 8 dg .. 8 dg + 7, stored transposed.  Keys past T
+  // are clamped to T-1: they lie above every query, so the mask removes them.
+  const int kg = tid & 15, dg = tid >> 4;
+  u32x4 kr[4], vr[4];
+  auto load_tile = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid * 4 + i;
-      const int key = c >> 4, chunk = c & 15;
-      const int kk = min(kv0 + key, T - 1);
-      store16(Ks + kswz(key, chunk), load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + chunk * 8));
+      const int kk = min(kv0 + (c >> 4), T - 1);
+      kr[i] = load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + (c & 15) * 8);
+      vr[i] = load16(v + static_cast<int64_t>(min(kv0 + 4 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
     }
-    // V tile, transposed: thread holds keys 4 kg .. 4 kg + 3, dims 8 dg .. 8 dg + 7.
-    {
-      const int kg = tid & 15, dg = tid >> 4;
-      u32x4 r[4];
+  };
+  auto store_tile = [&]() {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        r[i] = load16(v + static_cast<int64_t>(min(kv0 + 4 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t e[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = (j & 1) ? hi16(r[i][j >> 1]) : lo16(r[i][j >> 1]);
-        uint2 packed;
-        packed.x = e[0] | (e[1] << 16);
-        packed.y = e[2] | (e[3] << 16);
-        *reinterpret_cast<uint2*>(Vt + (8 * dg + j) * VT_STRIDE + 4 * kg) = packed;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid * 4 + i;
+      store16(Ks + kswz(c >> 4, c & 15), kr[i]);
     }
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t e[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = (j & 1) ? hi16(vr[i][j >> 1]) : lo16(vr[i][j >> 1]);
+      uint2 packed;
+      packed.x = e[0] | (e[1] << 16);
+      packed.y = e[2] | (e[3] << 16);
+      *reinterpret_cast<uint2*>(Vt + (8 * dg + j) * VT_STRIDE + 4 * kg) = packed;
+    }
+  };
+  load_tile(0);
+  store_tile();
+  __syncthreads();
+  for (int kv0 = 0; kv0 < kv_end; kv0 += FA_BKV) {
+    const bool more = kv0 + FA_BKV < kv_end;
+    if (more) load_tile(kv0 + FA_BKV);
 
     if (kv0 <= qw + 31) {  // some key of the tile is visible to some query of the wave
       // S^T: rows = keys kv0 + 32 kb + 8 (e / 4) + 4 half + e % 4, column = my_q.
@@ -218,35 +236,45 @@ __global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* _
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
         }
       }
+      // Causal mask, only on tiles that reach past the wave's first query.
+      if (kv0 + FA_BKV - 1 > qw) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kv0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) > my_q) s[kb][e] = -INFINITY;
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-          const float x = key > my_q ? -INFINITY : s[kb][e] * scale_log2;
-          s[kb][e] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m, mt);  // finite: key kv0 = 0 is visible to every query
-      const float alpha = exp2f(m - m_new);
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;  // the tile's max, in log2 units
+      // Lazy rescaling: the reference max m only moves when the tile's max
+      // exceeds it by more than 8, so every p = 2^(s - m) stays <= 2^8 and the
+      // rescale of O and l is skipped on most tiles.  O / l does not depend on
+      // m.  m is finite after the first tile: key 0 is visible to every query.
+      if (__ballot(mt > m + 8.f)) {
+        const float m_new = mt > m + 8.f ? mt : m;
+        const float alpha = exp2f(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        m = m_new;
+      }
       float lt = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(s[kb][e] - m_new);
+          const float p = exp2f(fmaf(s[kb][e], scale_log2, -m));
           s[kb][e] = p;
           lt += p;
         }
       lt += __shfl_xor(lt, 32);
-      l = l * alpha + lt;
-      m = m_new;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      l += lt;
       // O^T += V^T P^T over four 16-key steps.  Step j takes accumulator
       // entries e = 8 (j & 1) .. +7 of block j >> 1: for lane half q these are
       // keys base + 0..3 and base + 8..11 with base = 32 (j>>1) + 16 (j&1) + 4q,
@@ -256,7 +284,7 @@ __global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* _
         const int kb = j >> 1, hf = j & 1;
         u32x4 pw;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) pw[t] = pack_bf16x2(s[kb][8 * hf + 2 * t], s[kb][8 * hf + 2 * t + 1]);
+        for (int t = 0; t < 4; ++t) pw[t] = cvt_pk_bf16(s[kb][8 * hf + 2 * t], s[kb][8 * hf + 2 * t + 1]);
         const bf16x8 pb = as_bf16x8(pw);
         const int base = kb * 32 + hf * 16 + 4 * half;
 #pragma unroll
@@ -274,6 +302,10 @@ __global__ __launch_bounds__(FA_NT) void flash_attn_fwd_kernel(const uint16_t* _
       }
     }
     __syncthreads();
+    if (more) {
+      store_tile();
+      __syncthreads();
+    }
   }
 
   // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4.
