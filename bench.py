@@ -45,7 +45,8 @@ def kernel_source(kernel: str, T: int) -> str:
     """Source file of the kernel that runs as `kernel` at T tokens (bf16)."""
     if kernel in ("expert_up", "expert_down"):
         return "expert_stream.hip" if T <= 64 else "expert_gemm.hip"
-    return {"router": "router.hip", "dispatch": "dispatch.hip", "combine": "combine.hip"}[kernel]
+    return {"router": "router.hip", "dispatch": "dispatch.hip", "combine": "combine.hip",
+            "flash_attn": "attention.hip"}[kernel]
 
 
 # rocprofv3 kernel names -> step names
@@ -53,7 +54,9 @@ KERNEL_PATTERNS = [
     (r"stream_ffn_bf16_kernel<.*true>", "expert_up"), (r"stream_ffn_bf16_kernel<.*false>", "expert_down"),
     (r"gemm_bf16_kernel<true>", "expert_up"), (r"gemm_bf16_kernel<false>", "expert_down"),
     (r"router_top2_kernel", "router"), (r"dispatch_kernel", "dispatch"), (r"combine_kernel", "combine"),
+    (r"flash_attn_fwd_kernel", "flash_attn"),
 ]
+ATTN_WORKLOAD = "mixtral_attention_t4096"
 
 
 def _hip():
@@ -123,7 +126,7 @@ def traffic_from(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: 
     --pmc runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch) of the bench and of
     the copy probe (1 GiB read + 1 GiB written, which calibrates each counter)."""
     from synth import CONFIGS
-    cfg = CONFIGS[workload]
+    T, steps = (4096, ["flash_attn"]) if workload == ATTN_WORKLOAD else (CONFIGS[workload].T, KERNELS)
     f_scale = COPY_PROBE_BYTES / (_copy_kib(copy_fetch_csv, "FETCH_SIZE") * 1024)
     w_scale = COPY_PROBE_BYTES / (_copy_kib(copy_write_csv, "WRITE_SIZE") * 1024)
     fetch, write = _counter_avgs(fetch_csv), _counter_avgs(write_csv)
@@ -132,14 +135,14 @@ def traffic_from(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: 
     except (OSError, ValueError):
         out = {}
     entries = {}
-    for step in KERNELS:
+    for step in steps:
         if (step, "FETCH_SIZE") not in fetch or (step, "WRITE_SIZE") not in write:
             continue
         rb = fetch[(step, "FETCH_SIZE")] * 1024 * f_scale
         wb = write[(step, "WRITE_SIZE")] * 1024 * w_scale
         entries[step] = {"bytes_per_launch": round(rb + wb), "read_bytes": round(rb), "write_bytes": round(wb),
                          "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-                         "src_sha": _src_sha(kernel_source(step, cfg.T))}
+                         "src_sha": _src_sha(kernel_source(step, T))}
     out[workload] = entries
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
@@ -370,7 +373,7 @@ def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: 
         "sublayer_tflops": round((core_flops + proj_flops) / (sub_ms * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "kernel": "flash_attn", "achieved": round(core_tf, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(core_tf / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel_ms": round(core_ms, 4)},
+                     "traffic": _traffic(ATTN_WORKLOAD, "flash_attn", T), "kernel_ms": round(core_ms, 4)},
         "decoder_layer": {"ms": round(layer_ms, 4), "tokens_per_s": round(T / (layer_ms * 1e-3), 1),
                           "tflops": round((core_flops + proj_flops + moe_flops) / (layer_ms * 1e-3) / 1e12, 2)},
     }
@@ -457,6 +460,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true", help="skip the small-T decode latency sweep")
     ap.add_argument("--no-attention", action="store_true", help="skip the attention sublayer workload")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="measure only the attention sublayer workload and print its JSON")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write profiles/traffic.json for --config from rocprofv3 --pmc CSVs (no GPU needed)")
@@ -487,6 +492,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}), flush=True)
+        return
+    if a.attention_only:
+        print(json.dumps(measure_attention(a.steps)), flush=True)
         return
     cfg = CONFIGS[a.config]
     res = measure(cfg, a.steps, a.warmup)
