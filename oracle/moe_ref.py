@@ -65,8 +65,15 @@ def router_logits(x, w_gate, bias=None, dtype=np.float32) -> np.ndarray:
 
     The optional per-expert bias is the Linear bias of the router ([MIX-IN]
     "Router: Linear(emb_size -> num_experts)").
+
+    The pages fix the router's precision (fp32), not a summation order, so
+    the fp32 logit is taken to be the fp32 value of the exact dot product:
+    every product of a bf16 / fp32 input with an fp32 weight is exact in
+    fp64, the sum is formed in fp64 and rounded once.  The bias is then added
+    in fp32.
     """
-    g = widen(x, dtype) @ widen(w_gate, dtype).T
+    g = widen(x, np.float64) @ widen(w_gate, np.float64).T
+    g = g.astype(dtype)
     if bias is not None:
         g = g + widen(bias, dtype)
     return g.astype(dtype, copy=False)

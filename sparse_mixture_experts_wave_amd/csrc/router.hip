@@ -14,6 +14,11 @@
 // uses one token per workgroup
 // so that T workgroups share the work.
 //
+// Precision: every product x_j * W[e][j] (bf16 or fp32 times fp32) is exact
+// in fp64, and the sums are kept in fp64 until the logit is rounded once to
+// fp32, so the logit is the fp32 value of the exact dot product whatever the
+// summation order (the pages fix the router's precision, fp32, not an order).
+//
 // With gamma != nullptr the kernel also applies RMSNorm: it accumulates
 // sum(x^2) next to the dot products, and since u = x * rinv * gamma the
 // logits are rinv * sum_j (x_j gamma_j) W[e][j]; the normalised rows u are
@@ -57,8 +62,8 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
   constexpr int P = TPB * E;                   // logits per workgroup (<= 64)
   constexpr int COLS = P + (NORM ? TPB : 0);   // + sum of squares per token
   constexpr int LD = COLS + 1;                 // padded LDS row
-  __shared__ float red[4][64 * LD];
-  __shared__ float part[4][COLS];
+  __shared__ double red[4][64 * LD];
+  __shared__ double part[4][COLS];
   __shared__ float rinv_s[TPB];
 
   const int lane = threadIdx.x & 63;
@@ -68,13 +73,13 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
   const int cbeg = wave * quarter;
   const int cend = cbeg + quarter;
 
-  float acc[TPB][E];
-  float ss[TPB];
+  double acc[TPB][E];
+  double ss[TPB];
 #pragma unroll
   for (int t = 0; t < TPB; ++t) {
-    ss[t] = 0.f;
+    ss[t] = 0.0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[t][e] = 0.f;
+    for (int e = 0; e < E; ++e) acc[t][e] = 0.0;
   }
 
   for (int base = cbeg; base < cend; base += 512) {
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
         for (int t = 0; t < TPB; ++t)
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            ss[t] += xv[t][i] * xv[t][i];
+            ss[t] += static_cast<double>(xv[t][i]) * xv[t][i];
             xv[t][i] *= gv[i];
           }
       }
@@ -110,13 +115,13 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
 #pragma unroll
         for (int t = 0; t < TPB; ++t)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[t][e] += xv[t][i] * wv[i];
+          for (int i = 0; i < 8; ++i) acc[t][e] = fma(static_cast<double>(xv[t][i]), static_cast<double>(wv[i]), acc[t][e]);
       }
     }
   }
 
   // Column sums over the 64 lanes of each wave, then over the four waves.
-  float* r = red[wave];
+  double* r = red[wave];
 #pragma unroll
   for (int t = 0; t < TPB; ++t) {
 #pragma unroll
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
   }
   __syncthreads();
   if (lane < COLS) {
-    float s = 0.f;
+    double s = 0.0;
     for (int l = 0; l < 64; ++l) s += r[l * LD + lane];
     part[wave][lane] = s;
   }
@@ -135,11 +140,12 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
     const int j = lane < P ? lane : P - 1;  // idle lanes mirror the last column
     const int tl = j / E;
     const int e = j % E;
-    float g = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    const double gd = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    float g = static_cast<float>(gd);
     if constexpr (NORM) {
-      const float sq = part[0][P + tl] + part[1][P + tl] + part[2][P + tl] + part[3][P + tl];
+      const float sq = static_cast<float>(part[0][P + tl] + part[1][P + tl] + part[2][P + tl] + part[3][P + tl]);
       const float rinv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
-      g *= rinv;
+      g = static_cast<float>(gd * rinv);
       if (lane < P && e == 0) rinv_s[tl] = rinv;
     }
     if (bias != nullptr) g += bias[e];
@@ -219,14 +225,15 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
 }
 
 // Small T: one token per workgroup (T workgroups); large T: as many tokens
-// per workgroup as fit 64 logits (at most 8), so router weights are reused.
+// per workgroup as fit 32 logits (at most 4), so router weights are reused
+// and the fp64 partial sums of two workgroups fit one CU's LDS.
 constexpr int64_t kRouterOneTokenMaxT = 2048;
 
 template <int E, bool XBF16, bool NORM>
 hipError_t launch_e(const void* x, const float* wg, const float* bias, const float* gamma,
                     float eps, void* u_out, float* logits, int32_t* idx, float* w, int64_t T,
                     int d, int k, hipStream_t s) {
-  constexpr int TPB = (64 / E) < 8 ? (64 / E) : 8;
+  constexpr int TPB = (32 / E) < 1 ? 1 : ((32 / E) < 4 ? (32 / E) : 4);
   if (T <= kRouterOneTokenMaxT) {
     router_top2_kernel<E, 1, XBF16, NORM><<<static_cast<unsigned>(T), 256, 0, s>>>(
         x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d, k);

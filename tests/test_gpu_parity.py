@@ -282,7 +282,8 @@ def test_block_forward_two_layers_teacher_forced():
 # Mixtral shapes
 # ---------------------------------------------------------------------------
 def _mixtral_case(name, sample):
-    cfg = CONFIGS[name]
+    cfg = CONFIGS[name] if isinstance(name, str) else name
+    name = cfg.name
     say(f"mixtral {name}: generating")
     dv = generate_torch(cfg, torch.device("cuda:0"))
     x, wg, b = dv["x"], dv["w_gate"], dv["bias"]
@@ -336,6 +337,14 @@ def test_mixtral_prefill_t4096_sampled():
 
 def test_mixtral_skewed_t16384_sampled():
     _mixtral_case("mixtral_skewed_t16384", _sample_tokens)
+
+
+def test_mixtral_prefill_t65536_sampled():
+    """The largest size tested: 131072 dispatched rows, a grid of ~58k GEMM
+    workgroups; every token's routing and the permutation are checked, outputs
+    on sampled tokens."""
+    cfg = CONFIGS["mixtral_prefill_t4096"].with_(name="mixtral_prefill_t65536", cfg_id=30, T=65536)
+    _mixtral_case(cfg, _sample_tokens)
 
 
 def test_mixtral_stack_layers_teacher_forced():
