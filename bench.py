@@ -356,11 +356,14 @@ def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: 
     ones = torch.ones(cfg.d, dtype=torch.float32, device=dev)
 
     def layer():
+        # Every step starts from the same residual stream (a 32 MiB device copy,
+        # ~0.4 % of the step): applying the layer to its own output again and
+        # again lets h drift and the routing with it.
+        h.copy_(h0)
         moe.moe_attention_block_forward(h, gamma, 1e-5, wqkv, wo, H, G, theta, 0, ws)
         moe.moe_block_forward(h, ones, 1e-5, mw["w_gate"], mw["bias"], mw["w1"], mw["w3"], mw["w2"],
                               workspace=mws)
 
-    h.copy_(h0)
     layer_ms = timed(layer, max(3, steps // 2))
     core_flops = 2.0 * 2 * dh * H * T * (T + 1) / 2       # Q K^T and P V over the causal triangle
     proj_flops = 2.0 * T * d * (H + 2 * G) * dh + 2.0 * T * H * dh * d
