@@ -75,10 +75,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) (vmcnt, expcnt left unconstrained).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// A barrier that the compiler may not move any instruction across.
+// A barrier that the compiler may move no instruction across, LDS accesses
+// included: the s_barrier builtin is not a memory barrier for the optimizer,
+// which could otherwise hoist an operand read above the barrier that
+// publishes its slice.  No wait is emitted: each wave has already waited
+// (s_waitcnt) for the copies it publishes.
 __device__ __forceinline__ void bar() {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
+  asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
