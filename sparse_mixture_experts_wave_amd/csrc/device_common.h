@@ -39,6 +39,25 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// A raw buffer descriptor over [base, base + 4 GiB).  base must be the same in
+// every lane of the wave; reading it through readfirstlane keeps the
+// descriptor in scalar registers.  (Both halves are widened as unsigned: a
+// sign-extended low half would corrupt the high half of the address.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* base) {
+  const uint64_t bits = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits >> 32)));
+  // Raw buffer: stride 0, num_records = 4 GiB - 1 bytes, 32-bit data format word.
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), (short)0,
+                                           static_cast<int>(0xFFFFFFFFu), 0x00020000);
+}
+
+// A 16-byte buffer load at byte offset voff + soff (soff wave-uniform) with the
+// non-temporal cache policy: for data read once, such as streamed weights.
+__device__ __forceinline__ u32x4 load16_buf_nt(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2));
+}
+
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // SiLU(z) = z / (1 + e^{-z}).

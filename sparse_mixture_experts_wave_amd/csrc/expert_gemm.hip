@@ -286,19 +286,6 @@ __device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32
   if (grp == 0) bar();  // ... and group 0 ends one interval late: same barrier count
 }
 
-// A buffer descriptor over [base, base + 4 GiB).  base is the same in every
-// lane of the wave; reading it through readfirstlane keeps the descriptor in
-// scalar registers.  (Both halves are widened as unsigned: a sign-extended low
-// half would corrupt the high half of the address.)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const void* base) {
-  const uint64_t bits = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits)));
-  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bits >> 32)));
-  // Raw buffer: stride 0, num_records = 4 GiB - 1 bytes, 32-bit data format word.
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), (short)0,
-                                           static_cast<int>(0xFFFFFFFFu), 0x00020000);
-}
-
 template <bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
