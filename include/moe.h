@@ -92,11 +92,15 @@ typedef struct {
 
 /* Bytes of workspace moe_forward and moe_block_forward need (256-byte
  * aligned sub-buffers: routing, permutation, h [T*k][d_ff] in wt, y_sorted
- * [T*k][d] fp32, and for the block form the normalised input).  Returns 0
- * for an invalid shape.  Host only. */
+ * [T*k][d] fp32, for the block form the normalised input, and when the bf16
+ * grouped GEMM runs (T > 64) a fixed 64 MiB of fp32 partial sums: the last
+ * round of GEMM tiles is split along K over the idle CUs and summed in a
+ * fixed order, so results stay deterministic).  Returns 0 for an invalid
+ * shape.  Host only. */
 size_t moe_workspace_size(const moe_shape* shape);
 
-/* Bytes of workspace moe_expert_ffn needs (h only).  Host only. */
+/* Bytes of workspace moe_expert_ffn needs (h, then the GEMM partial sums as
+ * above).  Host only. */
 size_t moe_expert_ffn_workspace_size(const moe_shape* shape);
 
 /* Router: logits g = x W_g^T (+ bias), the k largest per token (k <= 8) and
@@ -194,8 +198,10 @@ typedef struct {
   int32_t act;  /* moe_dtype of activations and weights: BF16 is implemented */
 } moe_attn_shape;
 
-/* Bytes of workspace moe_attention_block_forward needs.  0 for an invalid
- * or unsupported shape.  Host only. */
+/* Bytes of workspace moe_attention_block_forward needs (normalised input,
+ * projections, rotated heads, attention output and, for T > 64, the GEMM
+ * partial sums as for moe_workspace_size).  0 for an invalid or unsupported
+ * shape.  Host only. */
 size_t moe_attention_workspace_size(const moe_attn_shape* shape);
 
 /* Causal GQA attention core on rotated heads:

@@ -105,18 +105,18 @@ hipError_t launch_expert_up_bf16(const uint16_t* x, const int32_t* expert_offset
                                  const int32_t* sorted_token, const uint16_t* w1,
                                  const uint16_t* w3, const uint16_t* b1, const uint16_t* b3,
                                  uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
-                                 hipStream_t stream) {
+                                 float* part, hipStream_t stream) {
   if (stream_supported(T, d, d_ff))
     return launch_stream_up_bf16(x, expert_offsets, sorted_token, w1, w3, b1, b3, h, T, d, d_ff, E, stream);
-  return launch_gemm_up_bf16(x, expert_offsets, sorted_token, w1, w3, b1, b3, h, T, k, d, d_ff, E, stream);
+  return launch_gemm_up_bf16(x, expert_offsets, sorted_token, w1, w3, b1, b3, h, T, k, d, d_ff, E, part, stream);
 }
 
 hipError_t launch_expert_down_bf16(const uint16_t* h, const int32_t* expert_offsets,
                                    const uint16_t* w2, const uint16_t* b2, float* y_sorted, int64_t T,
-                                   int k, int d, int d_ff, int E, hipStream_t stream) {
+                                   int k, int d, int d_ff, int E, float* part, hipStream_t stream) {
   if (stream_supported(T, d, d_ff))
     return launch_stream_down_bf16(h, expert_offsets, w2, b2, y_sorted, T, d, d_ff, E, stream);
-  return launch_gemm_down_bf16(h, expert_offsets, w2, b2, y_sorted, T, k, d, d_ff, E, stream);
+  return launch_gemm_down_bf16(h, expert_offsets, w2, b2, y_sorted, T, k, d, d_ff, E, part, stream);
 }
 
 hipError_t launch_expert_up_f32(const float* x, const int32_t* expert_offsets,

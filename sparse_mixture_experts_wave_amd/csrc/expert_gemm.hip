@@ -47,6 +47,15 @@
 // Tile order.  Consecutive tile numbers walk one expert in groups of 8 column
 // tiles x all of its row tiles, so blocks that share a weight tile (or an
 // activation tile) are numbered together.
+//
+// The last round.  A workgroup fills a CU (all of its LDS), so tiles run in
+// rounds of one per CU; when the tile count is not a multiple of the CU count
+// the last round would leave CUs idle (the down projection at T = 4096 has
+// 2 full rounds and 48 tiles).  Given a partial-sum buffer, the R tiles of the
+// last round are each split along K into S = floor(CUs / R) pieces (whole
+// slice pairs, at most 8); a piece stores its fp32 accumulators, and a fix-up
+// kernel adds a tile's S partial sums in piece order (deterministic) and runs
+// the same epilogue.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -61,6 +70,8 @@ constexpr int NTHR = 512;  // 8 waves
 constexpr int NGROUP = 8;  // column tiles per tile-order group
 constexpr int SLICE = BM * BK;  // elements per operand slice
 constexpr int COPIES = 4;       // copy instructions per thread per slice
+constexpr int MAX_SPLIT = 8;    // K pieces per split tile
+constexpr int ACC_CHUNKS = 32;  // float4 chunks of one thread's 128 accumulators
 
 static_assert(2 * NS * SLICE * 2 <= 163840, "LDS ring exceeds 160 KiB");
 
@@ -286,15 +297,108 @@ __device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32
   if (grp == 0) bar();  // ... and group 0 ends one interval late: same barrier count
 }
 
+// Number of tiles (sum over experts of the row tiles, times NT).
+__device__ __forceinline__ int count_tiles(const int32_t* __restrict__ offsets, int E, int NT) {
+  int total = 0;
+  for (int e = 0; e < E; ++e) total += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
+  return total;
+}
+
+// Which tiles run whole and which are split: tiles [0, full) whole, the R
+// tiles after them in S pieces each (S = 1: none split).
+struct SplitPlan {
+  int full, R, S;
+};
+
+__device__ __forceinline__ SplitPlan split_plan(int total, int cus, int KT, bool can_split) {
+  SplitPlan p;
+  p.full = total / cus * cus;
+  p.R = total - p.full;
+  p.S = 1;
+  if (can_split && p.R > 0) p.S = min(min(cus / p.R, MAX_SPLIT), KT / 4);
+  if (p.S < 2) {
+    p.S = 1;
+    p.full = total;
+    p.R = 0;
+  }
+  return p;
+}
+
+// Epilogue of one tile: biases, then SiLU(gate) * up rounded to bf16 (up) or
+// fp32 (down).  32x32 accumulator layout: lane holds column lane%32 and rows
+// 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Gated: the W1 and W3
+// bias of the lane's one column.
+template <bool GATED>
+__device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4][2],
+                                           const uint16_t* __restrict__ bias0,
+                                           const uint16_t* __restrict__ bias1, void* __restrict__ out, int N) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
+  float bb[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = GATED ? t.n0 + wn * 32 + (lane & 31) : t.n0 + wn * 64 + nb * 32 + (lane & 31);
+    const uint16_t* bsrc = (GATED && nb == 1) ? bias1 : bias0;
+    bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= t.rows) continue;
+      const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
+      if constexpr (GATED) {
+        const int n = t.n0 + wn * 32 + (lane & 31);
+        if (n < N)
+          static_cast<uint16_t*>(out)[row + n] = f32_to_bf16(silu_fast(acc[mi][0][v] + bb[0]) * (acc[mi][1][v] + bb[1]));
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
+          if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v] + bb[nb];
+        }
+      }
+    }
+}
+
+// A thread's 128 accumulators as 32 float4 chunks, chunk c of thread i at
+// part[c * NTHR + i] of its piece: each chunk store is one coalesced 8 KiB.
+__device__ __forceinline__ void store_partial(float4* __restrict__ part, const f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = (mi * 2 + nb) * 4 + j;
+        part[c * NTHR + threadIdx.x] =
+            make_float4(acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1], acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3]);
+      }
+}
+
 template <bool GATED>
 __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
-    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int NT) {
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int NT,
+    float4* __restrict__ part, int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;  // output columns per tile
+  // Work unit -> tile (and K piece).  Units past the last one exit.
+  const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, part != nullptr);
+  const int L = blockIdx.x;
+  int tile = L, piece = -1;
+  if (L >= plan.full) {
+    const int u = L - plan.full;
+    if (u >= plan.R * plan.S) return;
+    tile = plan.full + u / plan.S;
+    piece = u;
+  }
   Tile t;
-  if (!map_tile(offsets, E, NT, COLS, blockIdx.x, t)) return;
+  if (!map_tile(offsets, E, NT, COLS, tile, t)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -331,6 +435,18 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     cs.off[j] = (static_cast<uint32_t>(row) * K + chunk * 8) * 2;
   }
 
+  // A piece covers slice pairs [p KP / S, (p + 1) KP / S) of the KP = KT / 2
+  // pairs (at least 2 pairs: S <= KT / 4).
+  int Kp = K;
+  if (piece >= 0) {
+    const int KP = K / (2 * BK);
+    const int p = piece % plan.S;
+    const int s0 = 2 * (p * KP / plan.S), s1 = 2 * ((p + 1) * KP / plan.S);
+#pragma unroll
+    for (int j = 0; j < COPIES; ++j) cs.off[j] += static_cast<uint32_t>(s0) * (BK * 2);
+    Kp = (s1 - s0) * BK;
+  }
+
   f32x16 acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -340,51 +456,84 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
       for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
 
   if (t.rows == BM)
-    mainloop<GATED, true>(cs, K, t.rows, acc);
+    mainloop<GATED, true>(cs, Kp, t.rows, acc);
   else
-    mainloop<GATED, false>(cs, K, t.rows, acc);
+    mainloop<GATED, false>(cs, Kp, t.rows, acc);
 
-  // Epilogue.  32x32 accumulator layout: lane holds column lane%32 and rows
-  // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Bias of each of the
-  // lane's columns (gated: the W1 and W3 bias of its one column).
-  float bb[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = GATED ? t.n0 + wn * 32 + (lane & 31) : t.n0 + wn * 64 + nb * 32 + (lane & 31);
-    const uint16_t* bsrc = (GATED && nb == 1) ? bias1 : bias0;
-    bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
-  }
+  if (piece >= 0)
+    store_partial(part + static_cast<int64_t>(piece) * ACC_CHUNKS * NTHR, acc);
+  else
+    store_tile<GATED>(t, acc, bias0, bias1, out, N);
+}
+
+// Fix-up of the split tiles: workgroup b sums the S partial sums of split tile
+// b in piece order and runs the tile's epilogue.  Same thread layout as the
+// GEMM kernel.
+template <bool GATED>
+__global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restrict__ offsets, int E,
+                                                          const uint16_t* __restrict__ bias0,
+                                                          const uint16_t* __restrict__ bias1,
+                                                          void* __restrict__ out, int N, int K, int NT,
+                                                          const float4* __restrict__ part, int cus) {
+  constexpr int COLS = GATED ? BNR / 2 : BNR;
+  const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, true);
+  if (static_cast<int>(blockIdx.x) >= plan.R) return;
+  Tile t;
+  if (!map_tile(offsets, E, NT, COLS, plan.full + blockIdx.x, t)) return;
+  f32x16 acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= t.rows) continue;
-      const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
-      if constexpr (GATED) {
-        const int n = t.n0 + wn * 32 + (lane & 31);
-        if (n < N)
-          static_cast<uint16_t*>(out)[row + n] = f32_to_bf16(silu_fast(acc[mi][0][v] + bb[0]) * (acc[mi][1][v] + bb[1]));
-      } else {
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
-          if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v] + bb[nb];
+      for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
+  for (int p = 0; p < plan.S; ++p) {
+    const float4* src = part + (static_cast<int64_t>(blockIdx.x) * plan.S + p) * ACC_CHUNKS * NTHR;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = src[((mi * 2 + nb) * 4 + j) * NTHR + threadIdx.x];
+          acc[mi][nb][4 * j] += v.x;
+          acc[mi][nb][4 * j + 1] += v.y;
+          acc[mi][nb][4 * j + 2] += v.z;
+          acc[mi][nb][4 * j + 3] += v.w;
         }
-      }
-    }
+  }
+  store_tile<GATED>(t, acc, bias0, bias1, out, N);
+}
+
+// Workgroups that run at once: one per CU (the LDS ring takes a CU's LDS),
+// capped at the pieces the partial-sum buffer holds.
+int concurrent_tiles() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = kGemmMaxPieces;
+  return cus < kGemmMaxPieces ? cus : kGemmMaxPieces;
 }
 
 template <bool GATED>
 hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const uint16_t* B0,
                   const uint16_t* B1, const uint16_t* bias0, const uint16_t* bias1, void* out, int64_t rows,
-                  int N, int K, int E, hipStream_t s) {
+                  int N, int K, int E, float* part, hipStream_t s) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const int NT = (N + COLS - 1) / COLS;
-  // Upper bound on the row tiles: sum_e ceil(n_e / BM) <= ceil(rows / BM) + E.
+  const int cus = concurrent_tiles();
+  // Upper bound on the row tiles: sum_e ceil(n_e / BM) <= ceil(rows / BM) + E;
+  // splitting adds at most cus work units (R * S <= cus).
   const int64_t tiles = ((rows + BM - 1) / BM + E) * NT;
-  gemm_bf16_kernel<GATED><<<static_cast<unsigned>(tiles), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0, bias1,
-                                                                         out, N, K, NT);
+  const int64_t units = part ? tiles + cus : tiles;
+  float4* p4 = reinterpret_cast<float4*>(part);
+  gemm_bf16_kernel<GATED><<<static_cast<unsigned>(units), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0,
+                                                                         bias1, out, N, K, NT, p4, cus);
+  const hipError_t err = hipGetLastError();
+  if (part == nullptr || err != hipSuccess) return err;
+  // The split tiles number at most cus / 2 (S >= 2).
+  gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2), NTHR, 0, s>>>(offsets, E, bias0, bias1, out, N, K, NT,
+                                                                           p4, cus);
   return hipGetLastError();
 }
 
@@ -393,14 +542,14 @@ hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offse
 hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
                                const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
-                               hipStream_t stream) {
-  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, T * k, d_ff, d, E, stream);
+                               float* part, hipStream_t stream) {
+  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, T * k, d_ff, d, E, part, stream);
 }
 
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
-                                 int E, hipStream_t stream) {
-  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, T * k, d, d_ff, E, stream);
+                                 int E, float* part, hipStream_t stream) {
+  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, T * k, d, d_ff, E, part, stream);
 }
 
 }  // namespace moe

@@ -24,14 +24,16 @@ hipError_t launch_dispatch(const int32_t* topk_idx, int64_t T, int k, int E,
 // launches: up (h = SiLU(x W1^T + b1) * (x W3^T + b3), [T*k][d_ff] bf16) and
 // down (y_sorted = h W2^T + b2, [T*k][d] fp32).  Each per-expert Linear bias
 // ([E][d_ff] or [E][d], weight dtype) may be null.  Small T streams the weights.
+// part: the GEMM path's partial-sum buffer (gemm_partial_bytes) or NULL, in
+// which case the last round of tiles is not split.
 hipError_t launch_expert_up_bf16(const uint16_t* x, const int32_t* expert_offsets,
                                  const int32_t* sorted_token, const uint16_t* w1,
                                  const uint16_t* w3, const uint16_t* b1, const uint16_t* b3,
                                  uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
-                                 hipStream_t stream);
+                                 float* part, hipStream_t stream);
 hipError_t launch_expert_down_bf16(const uint16_t* h, const int32_t* expert_offsets,
                                    const uint16_t* w2, const uint16_t* b2, float* y_sorted, int64_t T,
-                                   int k, int d, int d_ff, int E, hipStream_t stream);
+                                   int k, int d, int d_ff, int E, float* part, hipStream_t stream);
 
 // Same in fp32 (h is [T*k][d_ff] fp32).
 hipError_t launch_expert_up_f32(const float* x, const int32_t* expert_offsets,
@@ -62,10 +64,10 @@ hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, co
 hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,
                                const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
                                const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
-                               hipStream_t stream);
+                               float* part, hipStream_t stream);
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
-                                 int E, hipStream_t stream);
+                                 int E, float* part, hipStream_t stream);
 
 // Router load-balancing loss over [layers][T][E] logits (aux_loss.hip).
 int aux_loss_max_k();
@@ -89,5 +91,15 @@ hipError_t launch_row_range(int32_t* offsets, int64_t rows, hipStream_t stream);
 // Token count at or below which the bf16 expert FFN streams weights
 // (decode regime) instead of running the tiled grouped GEMM.
 constexpr int64_t kStreamMaxT = 64;
+
+// The grouped GEMM's partial-sum buffer: room for the K pieces of one round of
+// split tiles, at most kGemmMaxPieces pieces of 256 x 256 fp32.
+constexpr int kGemmMaxPieces = 256;
+constexpr size_t kGemmPartialBytes = static_cast<size_t>(kGemmMaxPieces) * 256 * 256 * 4;
+// Bytes of partial-sum buffer a bf16 expert FFN of this shape uses (0 when it
+// takes the streaming path).
+inline size_t gemm_partial_bytes(int64_t T, int d, int d_ff) {
+  return stream_supported(T, d, d_ff) ? 0 : kGemmPartialBytes;
+}
 
 }  // namespace moe

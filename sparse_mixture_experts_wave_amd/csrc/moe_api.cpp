@@ -92,8 +92,13 @@ size_t up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout of moe_forward / moe_block_forward.
 struct Layout {
-  size_t topk_idx, topk_w, offsets, sorted_token, inv_pos, h, y_sorted, u, total;
+  size_t topk_idx, topk_w, offsets, sorted_token, inv_pos, h, y_sorted, u, part, total;
 };
+
+// Partial-sum buffer of the bf16 grouped GEMM (0 bytes on the streaming path).
+size_t part_bytes(const moe_shape* s) {
+  return s->wt == MOE_BF16 ? moe::gemm_partial_bytes(s->T, s->d, s->d_ff) : 0;
+}
 
 Layout layout(const moe_shape* s, bool block) {
   const size_t rows = static_cast<size_t>(s->T) * s->k;
@@ -107,13 +112,14 @@ Layout layout(const moe_shape* s, bool block) {
   L.h = at; at += up(rows * s->d_ff * esize(s->wt));
   L.y_sorted = at; at += up(rows * s->d * 4);
   L.u = at; if (block) at += up(static_cast<size_t>(s->T) * s->d * esize(s->act));
+  L.part = at; at += up(part_bytes(s));
   L.total = at;
   return L;
 }
 
-size_t ffn_ws(const moe_shape* s) {
-  return up(static_cast<size_t>(s->T) * s->k * s->d_ff * esize(s->wt));
-}
+// moe_expert_ffn's workspace: h, then the partial-sum buffer.
+size_t ffn_h_bytes(const moe_shape* s) { return up(static_cast<size_t>(s->T) * s->k * s->d_ff * esize(s->wt)); }
+size_t ffn_ws(const moe_shape* s) { return ffn_h_bytes(s) + up(part_bytes(s)); }
 
 template <typename P>
 P* at(void* ws, size_t off) {
@@ -149,7 +155,7 @@ moe_status check_bias(const moe_expert_bias* eb) {
 
 moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const int32_t* st,
                    const void* w1, const void* w3, const void* w2, const moe_expert_bias* eb, float* y_sorted,
-                   void* h, void* stream, bool timed) {
+                   void* h, float* part, void* stream, bool timed) {
   const void* b1 = eb ? eb->b1 : nullptr;
   const void* b3 = eb ? eb->b3 : nullptr;
   const void* b2 = eb ? eb->b2 : nullptr;
@@ -158,7 +164,7 @@ moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const 
     err = moe::launch_expert_up_bf16(static_cast<const uint16_t*>(x), off, st, static_cast<const uint16_t*>(w1),
                                      static_cast<const uint16_t*>(w3), static_cast<const uint16_t*>(b1),
                                      static_cast<const uint16_t*>(b3), static_cast<uint16_t*>(h), s->T, s->k,
-                                     s->d, s->d_ff, s->E, hs(stream));
+                                     s->d, s->d_ff, s->E, part, hs(stream));
   } else {
     err = moe::launch_expert_up_f32(static_cast<const float*>(x), off, st, static_cast<const float*>(w1),
                                     static_cast<const float*>(w3), static_cast<const float*>(b1),
@@ -170,7 +176,7 @@ moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const 
   if (s->wt == MOE_BF16) {
     err = moe::launch_expert_down_bf16(static_cast<const uint16_t*>(h), off, static_cast<const uint16_t*>(w2),
                                        static_cast<const uint16_t*>(b2), y_sorted, s->T, s->k, s->d, s->d_ff,
-                                       s->E, hs(stream));
+                                       s->E, part, hs(stream));
   } else {
     err = moe::launch_expert_down_f32(static_cast<const float*>(h), off, static_cast<const float*>(w2),
                                       static_cast<const float*>(b2), y_sorted, s->T, s->k, s->d, s->d_ff, s->E,
@@ -205,7 +211,8 @@ moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, 
   MOE_TRY(mark(1, stream));
   MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
   MOE_TRY(mark(2, stream));
-  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, stream, true));
+  float* part = part_bytes(s) ? at<float>(ws, L.part) : nullptr;
+  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, part, stream, true));
   MOE_TRY(mark(4, stream));
   MOE_TRY(hip_status(moe::launch_combine(ys, inv, w, residual, y, s->act == MOE_BF16, s->T, s->k, s->d, hs(stream)),
                      "combine launch"));
@@ -234,7 +241,7 @@ moe_status check_attn_shape(const moe_attn_shape* s) {
 }
 
 struct AttnLayout {
-  size_t offsets, xn, qkv, q, k, v, o, oproj, total;
+  size_t offsets, xn, qkv, q, k, v, o, oproj, part, total;
 };
 
 AttnLayout attn_layout(const moe_attn_shape* s) {
@@ -250,6 +257,10 @@ AttnLayout attn_layout(const moe_attn_shape* s) {
   L.v = at; at += up(T * nkv * 2);
   L.o = at; at += up(T * nq * 2);
   L.oproj = at; at += up(T * s->d * 4);
+  // The projections' GEMM partial sums (one buffer, used by one projection at a time).
+  const size_t pb = std::max(moe::gemm_partial_bytes(s->T, static_cast<int>(nq + 2 * nkv), s->d),
+                             moe::gemm_partial_bytes(s->T, s->d, static_cast<int>(nq)));
+  L.part = at; at += up(pb);
   L.total = at;
   return L;
 }
@@ -316,7 +327,9 @@ moe_status moe_expert_ffn(const moe_shape* shape, const void* x, const int32_t* 
   MOE_TRY(need(ws, "ws"));
   if (ws_bytes < ffn_ws(shape))
     return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, ffn_ws(shape));
-  return run_ffn(shape, x, expert_offsets, sorted_token, w1, w3, w2, expert_bias, y_sorted, ws, stream, false);
+  float* part = part_bytes(shape) ? at<float>(ws, ffn_h_bytes(shape)) : nullptr;
+  return run_ffn(shape, x, expert_offsets, sorted_token, w1, w3, w2, expert_bias, y_sorted, ws, part, stream,
+                 false);
 }
 
 moe_status moe_combine(const moe_shape* shape, const float* y_sorted, const int32_t* inv_pos,
@@ -448,14 +461,15 @@ moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inou
   // The projections run on the experts' GEMM as a single expert owning all T rows.
   MOE_TRY(hip_status(moe::launch_row_range(off, T, st), "row range launch"));
   MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st), "rmsnorm launch"));
+  float* part = L.part < L.total ? at<float>(ws, L.part) : nullptr;
   MOE_TRY(hip_status(moe::launch_expert_down_bf16(xn, off, static_cast<const uint16_t*>(wqkv), nullptr, qkv, T, 1,
-                                                  nqkv, d, 1, st),
+                                                  nqkv, d, 1, part, st),
                      "qkv projection launch"));
   MOE_TRY(hip_status(moe::launch_rope_pack(qkv, q, k, v, T, H, G, dh, static_cast<double>(rope_theta), pos0, st),
                      "rope launch"));
   MOE_TRY(hip_status(moe::launch_flash_attn(q, k, v, o, T, H, G, dh, st), "attention launch"));
   MOE_TRY(hip_status(moe::launch_expert_down_bf16(o, off, static_cast<const uint16_t*>(wo), nullptr, oproj, T, 1, d,
-                                                  nq, 1, st),
+                                                  nq, 1, part, st),
                      "output projection launch"));
   return hip_status(moe::launch_residual_add(h, oproj, T * d, st), "residual launch");
 }

@@ -187,6 +187,29 @@ def test_expert_ffn(T, d, d_ff, dtype, path):
     assert err <= (F32_TOL if dtype == "f32" else BF16_TOL), err
 
 
+@pytest.mark.parametrize("d,d_ff,counts", [
+    (512, 1024, [1024, 1024]),         # up 64 tiles in 4 K pieces, down 16 tiles in 8
+    (1024, 2048, [300, 257, 1, 700]),  # ragged experts: up 128 tiles in 2 pieces, down 32 tiles in 8
+    (512, 4096, [1500, 1100]),         # up 352 tiles: 256 whole, 96 in 2 pieces; down 22 tiles in 8
+])
+def test_expert_ffn_split_last_round(d, d_ff, counts):
+    """The grouped GEMM splits the tiles of its last round along K (on a
+    256-CU part: the piece counts noted above) and sums the pieces in a
+    fix-up pass; rows are routed by hand so the tile counts are known."""
+    E, T = len(counts), sum(counts)
+    say(f"expert_ffn split d={d} d_ff={d_ff} counts={counts}")
+    inp = generate(small("split", T, d, d_ff, E=E))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    st = np.random.default_rng(T).permutation(T).astype(np.int32)
+    ref = oracle.expert_rows_ref(inp["x"], st, off, inp["w1"], inp["w3"], inp["w2"])
+    args = (to_dev(inp["x"]), to_dev(off), to_dev(st), to_dev(inp["w1"]), to_dev(inp["w3"]), to_dev(inp["w2"]))
+    ys = moe.moe_expert_ffn(*args, k=1).clone()
+    again = moe.moe_expert_ffn(*args, k=1)
+    torch.cuda.synchronize()
+    assert max_rel_err(to_host(ys), ref) <= BF16_TOL
+    assert torch.equal(ys, again)  # the pieces are summed in a fixed order
+
+
 # ---------------------------------------------------------------------------
 # the whole layer
 # ---------------------------------------------------------------------------
