@@ -328,10 +328,12 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int cus, int KT, bool
 // fp32 (down).  32x32 accumulator layout: lane holds column lane%32 and rows
 // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Gated: the W1 and W3
 // bias of the lane's one column.
+// Only the 32-row blocks mi in [mlo, mhi) of each wave are stored.
 template <bool GATED>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4][2],
                                            const uint16_t* __restrict__ bias0,
-                                           const uint16_t* __restrict__ bias1, void* __restrict__ out, int N) {
+                                           const uint16_t* __restrict__ bias1, void* __restrict__ out, int N,
+                                           int mlo = 0, int mhi = 4) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2;
@@ -348,7 +350,7 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (r >= t.rows) continue;
+      if (mi < mlo || mi >= mhi || r >= t.rows) continue;
       const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
       if constexpr (GATED) {
         const int n = t.n0 + wn * 32 + (lane & 31);
@@ -466,9 +468,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     store_tile<GATED>(t, acc, bias0, bias1, out, N);
 }
 
-// Fix-up of the split tiles: workgroup b sums the S partial sums of split tile
-// b in piece order and runs the tile's epilogue.  Same thread layout as the
-// GEMM kernel.
+// Fix-up of the split tiles: workgroup 4 b + mi sums, for 32-row block mi of
+// every wave, the S partial sums of split tile b in piece order and runs that
+// block's epilogue (four workgroups per tile spread the partial-sum reads over
+// more CUs).  Same thread layout as the GEMM kernel.
 template <bool GATED>
 __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restrict__ offsets, int E,
                                                           const uint16_t* __restrict__ bias0,
@@ -477,9 +480,11 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
                                                           const float4* __restrict__ part, int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, true);
-  if (static_cast<int>(blockIdx.x) >= plan.R) return;
+  const int b = blockIdx.x >> 2, mb = blockIdx.x & 3;
+  if (b >= plan.R) return;
   Tile t;
-  if (!map_tile(offsets, E, NT, COLS, plan.full + blockIdx.x, t)) return;
+  if (!map_tile(offsets, E, NT, COLS, plan.full + b, t)) return;
+  if (mb * 32 >= t.rows) return;  // no valid row in this block of either wave row
   f32x16 acc[4][2];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -488,9 +493,10 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
   for (int p = 0; p < plan.S; ++p) {
-    const float4* src = part + (static_cast<int64_t>(blockIdx.x) * plan.S + p) * ACC_CHUNKS * NTHR;
+    const float4* src = part + (static_cast<int64_t>(b) * plan.S + p) * ACC_CHUNKS * NTHR;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi != mb) continue;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -501,8 +507,9 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
           acc[mi][nb][4 * j + 2] += v.z;
           acc[mi][nb][4 * j + 3] += v.w;
         }
+    }
   }
-  store_tile<GATED>(t, acc, bias0, bias1, out, N);
+  store_tile<GATED>(t, acc, bias0, bias1, out, N, mb, mb + 1);
 }
 
 // Workgroups that run at once: one per CU (the LDS ring takes a CU's LDS),
@@ -525,15 +532,21 @@ hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offse
   // Upper bound on the row tiles: sum_e ceil(n_e / BM) <= ceil(rows / BM) + E;
   // splitting adds at most cus work units (R * S <= cus).
   const int64_t tiles = ((rows + BM - 1) / BM + E) * NT;
+  // Only a kernel of a few rounds ends in one synchronised partial round: over
+  // many rounds the tiles' durations differ, the rounds drift apart and the
+  // end is ragged anyway (measured: no gain at 15 rounds, 13-26 % at 1-3).  So
+  // with at least 4 rounds for certain (ceil(rows / BM) * NT tiles at least)
+  // nothing is split and the fix-up is not launched.
+  if (((rows + BM - 1) / BM) * NT >= 4 * static_cast<int64_t>(cus)) part = nullptr;
   const int64_t units = part ? tiles + cus : tiles;
   float4* p4 = reinterpret_cast<float4*>(part);
   gemm_bf16_kernel<GATED><<<static_cast<unsigned>(units), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0,
                                                                          bias1, out, N, K, NT, p4, cus);
   const hipError_t err = hipGetLastError();
   if (part == nullptr || err != hipSuccess) return err;
-  // The split tiles number at most cus / 2 (S >= 2).
-  gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2), NTHR, 0, s>>>(offsets, E, bias0, bias1, out, N, K, NT,
-                                                                           p4, cus);
+  // The split tiles number at most cus / 2 (S >= 2), four workgroups each.
+  gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2 * 4), NTHR, 0, s>>>(offsets, E, bias0, bias1, out, N, K,
+                                                                               NT, p4, cus);
   return hipGetLastError();
 }
 
