@@ -457,7 +457,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
 
-  if (t.rows == BM)
+  // Every 32-row slice holds at least one row once rows > BM - 32: the
+  // branch-free path then does the same MFMAs.
+  if (t.rows > BM - 32)
     mainloop<GATED, true>(cs, Kp, t.rows, acc);
   else
     mainloop<GATED, false>(cs, Kp, t.rows, acc);
