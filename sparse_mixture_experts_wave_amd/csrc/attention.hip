@@ -147,6 +147,11 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
+// 2^x with the hardware instruction alone (v_exp_f32): results below 2^-126
+// flush to zero instead of being rebuilt as denormals, which a softmax weight
+// that small never needs (exp2f would spend about six instructions on it).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const uint16_t* __restrict__ v,
@@ -256,7 +261,7 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       // m.  m is finite after the first tile: key 0 is visible to every query.
       if (__ballot(mt > m + 8.f)) {
         const float m_new = mt > m + 8.f ? mt : m;
-        const float alpha = exp2f(m - m_new);
+        const float alpha = exp2_fast(m - m_new);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(fmaf(s[kb][e], scale_log2, -m));
+          const float p = exp2_fast(fmaf(s[kb][e], scale_log2, -m));
           s[kb][e] = p;
           lt += p;
         }
