@@ -90,7 +90,12 @@ template <int E>
 hipError_t launch_e(const int32_t* idx, int64_t T, int k, int32_t* off, int32_t* st, int32_t* inv,
                     hipStream_t s) {
   constexpr int NT = (E <= 16) ? 1024 : (16384 / E);
-  dispatch_kernel<E, NT><<<1, NT, 0, s>>>(idx, static_cast<int>(T), k, off, st, inv);
+  // Few (token, slot) pairs (decode): a single wave, whose barriers cost
+  // nothing, instead of 16 waves that mostly count zeros.
+  if (T * k <= 256)
+    dispatch_kernel<E, 64><<<1, 64, 0, s>>>(idx, static_cast<int>(T), k, off, st, inv);
+  else
+    dispatch_kernel<E, NT><<<1, NT, 0, s>>>(idx, static_cast<int>(T), k, off, st, inv);
   return hipGetLastError();
 }
 

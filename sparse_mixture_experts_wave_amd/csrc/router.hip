@@ -3,12 +3,14 @@
 // формулах", MoE equation; "MoE изнутри", steps 1-2: Linear router, top-k,
 // softmax over the kept logits in float32.)
 //
-// A workgroup handles TPB tokens; its four waves split the row into
-// quarters.  Each lane walks its quarter in 8-element (16-byte bf16) chunks,
-// so a wave reads 1 KiB of a row per step, and every router weight chunk it
+// A workgroup handles TPB tokens; its NW waves split the row into NW equal
+// parts (NW = 8 for one token per workgroup and E <= 16, so each wave's
+// loads go out in a single pass; otherwise 4).  Each lane walks its part in
+// 8-element (16-byte bf16) chunks, so a wave reads 1 KiB of a row per step,
+// and every router weight chunk it
 // loads serves all TPB tokens.  The TPB x E partial dot products are
 // transposed through LDS: lane j of each wave sums column j over its 64
-// lanes, then wave 0 adds the four quarters, so lane j ends with the logit
+// lanes, then wave 0 adds the NW parts in order, so lane j ends with the logit
 // of (token j / E, expert j % E).  The top-k is a butterfly over the E lanes
 // of each token (E is a power of two), one round per kept expert.  Small T
 // uses one token per workgroup
@@ -53,8 +55,8 @@ __device__ __forceinline__ bool beats(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
 
-template <int E, int TPB, bool XBF16, bool NORM>
-__global__ __launch_bounds__(256) void router_top2_kernel(
+template <int E, int TPB, int NW, bool XBF16, bool NORM>
+__global__ __launch_bounds__(64 * NW) void router_top2_kernel(
     const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     const float* __restrict__ gamma, float eps, void* __restrict__ u_out,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -62,16 +64,16 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
   constexpr int P = TPB * E;                   // logits per workgroup (<= 64)
   constexpr int COLS = P + (NORM ? TPB : 0);   // + sum of squares per token
   constexpr int LD = COLS + 1;                 // padded LDS row
-  __shared__ double red[4][64 * LD];
-  __shared__ double part[4][COLS];
+  __shared__ double red[NW][64 * LD];
+  __shared__ double part[NW][COLS];
   __shared__ float rinv_s[TPB];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tok0 = blockIdx.x * TPB;
-  const int quarter = d >> 2;  // a multiple of 16
-  const int cbeg = wave * quarter;
-  const int cend = cbeg + quarter;
+  const int part_len = d / NW;  // a multiple of 8 (d % 64 == 0)
+  const int cbeg = wave * part_len;
+  const int cend = cbeg + part_len;
 
   double acc[TPB][E];
   double ss[TPB];
@@ -140,10 +142,15 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
     const int j = lane < P ? lane : P - 1;  // idle lanes mirror the last column
     const int tl = j / E;
     const int e = j % E;
-    const double gd = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+    double gd = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) gd += part[w][j];
     float g = static_cast<float>(gd);
     if constexpr (NORM) {
-      const float sq = static_cast<float>(part[0][P + tl] + part[1][P + tl] + part[2][P + tl] + part[3][P + tl]);
+      double sqd = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sqd += part[w][P + tl];
+      const float sq = static_cast<float>(sqd);
       const float rinv = 1.0f / sqrtf(sq / static_cast<float>(d) + eps);
       g = static_cast<float>(gd * rinv);
       if (lane < P && e == 0) rinv_s[tl] = rinv;
@@ -201,7 +208,7 @@ __global__ __launch_bounds__(256) void router_top2_kernel(
     __syncthreads();
     for (int t = 0; t < TPB && tok0 + t < T; ++t) {
       const float rt = rinv_s[t];
-      for (int col = threadIdx.x * 8; col < d; col += 256 * 8) {
+      for (int col = threadIdx.x * 8; col < d; col += 64 * NW * 8) {
         const int64_t off = static_cast<int64_t>(tok0 + t) * d + col;
         float xv[8];
         load_x8<XBF16>(x, off, xv);
@@ -235,11 +242,12 @@ hipError_t launch_e(const void* x, const float* wg, const float* bias, const flo
                     int d, int k, hipStream_t s) {
   constexpr int TPB = (32 / E) < 1 ? 1 : ((32 / E) < 4 ? (32 / E) : 4);
   if (T <= kRouterOneTokenMaxT) {
-    router_top2_kernel<E, 1, XBF16, NORM><<<static_cast<unsigned>(T), 256, 0, s>>>(
+    constexpr int NW = E <= 16 ? 8 : 4;  // fp64 transpose buffer: NW x 64 x (E + 1) doubles
+    router_top2_kernel<E, 1, NW, XBF16, NORM><<<static_cast<unsigned>(T), 64 * NW, 0, s>>>(
         x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d, k);
   } else {
     const dim3 grid(static_cast<unsigned>((T + TPB - 1) / TPB));
-    router_top2_kernel<E, TPB, XBF16, NORM><<<grid, 256, 0, s>>>(
+    router_top2_kernel<E, TPB, 4, XBF16, NORM><<<grid, 256, 0, s>>>(
         x, wg, bias, gamma, eps, u_out, logits, idx, w, static_cast<int>(T), d, k);
   }
   return hipGetLastError();
