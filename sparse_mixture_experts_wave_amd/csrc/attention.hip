@@ -88,12 +88,15 @@ __global__ __launch_bounds__(256) void rope_pack_kernel(const float* __restrict_
   sincos(ang, &sd, &cd);
   const float c = static_cast<float>(cd), s = static_cast<float>(sd);
   const float* row = qkv + t * static_cast<int64_t>(H + 2 * G) * dh + 2 * i;
+  // Unrolled so that several heads' loads are in flight at once.
+#pragma unroll 8
   for (int hh = 0; hh < H + G; ++hh) {
     const float2 x = *reinterpret_cast<const float2*>(row + static_cast<int64_t>(hh) * dh);
     const uint32_t r = pack_bf16x2(x.x * c - x.y * s, x.x * s + x.y * c);
     uint16_t* dst = hh < H ? q + (t * H + hh) * dh : k + (t * G + (hh - H)) * dh;
     *reinterpret_cast<uint32_t*>(dst + 2 * i) = r;
   }
+#pragma unroll 8
   for (int gg = 0; gg < G; ++gg) {
     const float2 x = *reinterpret_cast<const float2*>(row + static_cast<int64_t>(H + G + gg) * dh);
     *reinterpret_cast<uint32_t*>(v + (t * G + gg) * dh + 2 * i) = pack_bf16x2(x.x, x.y);
