@@ -327,6 +327,237 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 }
 
+// ---------------------------------------------------------------------------
+// causal GQA flash attention, software-pipelined per wave
+// ---------------------------------------------------------------------------
+// Eight waves (two per SIMD) of 32 queries each share 64-key K / V tiles.  Per
+// tile j a wave runs, in order:
+//   A: S(j+1) for keys 0..31 of tile j+1 (8 MFMAs) beside tile j's row max;
+//   (the lazy-rescale branch, rarely taken);
+//   B: S(j+1) for keys 32..63 beside exp / sum / bf16 packing of tile j's
+//      keys 0..31;
+//   C: O(j) for keys 0..31 (8 MFMAs) beside the same for keys 32..63;
+//   D: O(j) for keys 32..63 beside the stores of the next tiles into LDS.
+// So the matrix core always has MFMAs that do not wait on the softmax.  K and
+// V^T have two LDS buffers each: while tile j is consumed, K(j+2) goes into the
+// buffer K(j) used and V(j+1) into the buffer V(j-1) used, so one barrier per
+// tile suffices.
+constexpr int F2_NW = 8;                   // waves per workgroup
+constexpr int F2_QW = 32;                  // queries per wave
+constexpr int F2_BQ = F2_QW * F2_NW;       // queries per workgroup
+constexpr int F2_NT = 64 * F2_NW;
+constexpr int F2_LD = FA_D + 8;            // padded K / Q row: 272 bytes
+constexpr int F2_KC = FA_BKV * FA_D / 8 / F2_NT;  // 16-byte K chunks per thread per tile (2)
+
+// K rows padded to 272 bytes: the 16 rows one operand read touches start
+// 4 banks apart (conflict-free), and every chunk of a lane's row is a constant
+// offset from one address.
+__device__ __forceinline__ int kpad(int row, int chunk) { return row * F2_LD + chunk * 8; }
+
+__global__ __launch_bounds__(F2_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd2_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, int T, int H, int G, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BKV * F2_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][FA_D * VT_STRIDE];
+
+  const int h = blockIdx.x;
+  const int n_qt = (T + F2_BQ - 1) / F2_BQ;
+  const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * F2_BQ;  // longest rows first
+  const int g = h / (H / G);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int qw = q0 + wave * F2_QW;        // first query of the wave
+  const int my_q = qw + (lane & 31);       // the lane's query: its column of S^T and O^T
+  const int64_t ld_q = static_cast<int64_t>(H) * FA_D;
+  const int64_t ld_kv = static_cast<int64_t>(G) * FA_D;
+
+  // B operand of S^T = K Q^T: lane holds query my_q (clamped to T - 1; its
+  // output is not stored), dims 16 ks + 8 half .. +7.
+  bf16x8 qf[8];
+  {
+    const uint16_t* qp = q + static_cast<int64_t>(min(my_q, T - 1)) * ld_q + h * FA_D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(load16(qp + 16 * ks));
+  }
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = min(T, q0 + F2_BQ);
+  const int ntiles = (kv_end + FA_BKV - 1) / FA_BKV;
+  // K/V staging through registers.  K: chunks c = KC tid + i, row c / 16.
+  // V: keys 2 kg, 2 kg + 1 (kg = tid % 32) x dims 8 dg .. 8 dg + 7
+  // (dg = tid / 32), stored transposed.  Keys past T are clamped to T - 1:
+  // they lie above every query, so the mask removes them.
+  const int kg = tid & 31, dg = tid >> 5;
+  u32x4 kr[F2_KC], vr[2];
+  auto load_k = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < F2_KC; ++i) {
+      const int c = tid * F2_KC + i;
+      const int kk = min(kv0 + (c >> 4), T - 1);
+      kr[i] = load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + (c & 15) * 8);
+    }
+  };
+  auto load_v = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      vr[i] = load16(v + static_cast<int64_t>(min(kv0 + 2 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < F2_KC; ++i) {
+      const int c = tid * F2_KC + i;
+      store16(&Ks[buf][kpad(c >> 4, c & 15)], kr[i]);
+    }
+  };
+  auto store_v = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e0 = (j & 1) ? hi16(vr[0][j >> 1]) : lo16(vr[0][j >> 1]);
+      const uint32_t e1 = (j & 1) ? hi16(vr[1][j >> 1]) : lo16(vr[1][j >> 1]);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dg + j) * VT_STRIDE + 2 * kg]) = e0 | (e1 << 16);
+    }
+  };
+  // S^T of keys 32 kb .. 32 kb + 31 of the tile in buffer buf: rows = keys
+  // 32 kb + 8 (e / 4) + 4 half + e % 4, column = my_q.
+  auto s_half = [&](f32x16 (&s)[2], int buf, int kb) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
+    bf16x8 a[8];  // all eight operand reads first, so the MFMAs do not wait on each
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a[ks] = as_bf16x8(load16(&Ks[buf][kpad(kb * 32 + (lane & 31), 2 * ks + half)]));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], s[kb], 0, 0, 0);
+  };
+  // p = 2^(s scale - m) for keys 32 kb .. + 31, their sum into lt, and the bf16
+  // B operands of O^T += V^T P^T for the two 16-key steps of kb.
+  auto softmax_half = [&](const f32x16 (&s)[2], int kb, float& lt, u32x4 (&pw)[2]) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = 8 * hf + 2 * t;
+        const float p0 = exp2_fast(fmaf(s[kb][e], scale_log2, -m));
+        const float p1 = exp2_fast(fmaf(s[kb][e + 1], scale_log2, -m));
+        lt += p0 + p1;
+        pw[hf][t] = cvt_pk_bf16(p0, p1);
+      }
+  };
+  // O^T += V^T P^T over the two 16-key steps of keys 32 kb .. + 31.  Step hf
+  // takes accumulator entries e = 8 hf .. +7, i.e. for lane half q the keys
+  // base + 0..3 and base + 8..11 with base = 32 kb + 16 hf + 4 q, and the A
+  // operand reads V^T at exactly those keys.
+  auto o_half = [&](int buf, int kb, const u32x4 (&pw)[2]) {
+    u32x4 aw[2][4];  // all operand reads first
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int base = kb * 32 + hf * 16 + 4 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint16_t* vp = &Vt[buf][(db * 32 + (lane & 31)) * VT_STRIDE + base];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+        aw[hf][db][0] = lo.x;
+        aw[hf][db][1] = lo.y;
+        aw[hf][db][2] = hi.x;
+        aw[hf][db][3] = hi.y;
+      }
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aw[hf][db]), as_bf16x8(pw[hf]), oacc[db], 0, 0, 0);
+  };
+
+  // One tile: sc holds S^T of tile j, sn receives S^T of tile j + 1.
+  auto tile = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int kv0 = j * FA_BKV;
+    const int buf = j & 1;
+    if (j + 2 < ntiles) load_k(kv0 + 2 * FA_BKV);
+    if (j + 1 < ntiles) load_v(kv0 + FA_BKV);
+    if (kv0 <= qw + F2_QW - 1) {  // some key of tile j is visible to some query of the wave
+      if (kv0 + FA_BKV - 1 > qw) {  // causal mask on the diagonal tiles only
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kv0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) > my_q) sc[kb][e] = -INFINITY;
+      }
+      // A: S(j+1), keys 0..31, beside the row max of tile j.
+      s_half(sn, buf ^ 1, 0);
+      float x = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x = fmaxf(x, sc[kb][e]);
+      const float mt = fmaxf(x, __shfl_xor(x, 32)) * scale_log2;
+      // Lazy rescaling: the reference max m only moves when the tile's max
+      // exceeds it by more than 8, so every p = 2^(s - m) stays <= 2^8 and the
+      // rescale of O and l is skipped on most tiles.  O / l does not depend on
+      // m.  m is finite after the first tile: key 0 is visible to every query.
+      if (__ballot(mt > m + 8.f)) {
+        const float m_new = mt > m + 8.f ? mt : m;
+        const float alpha = exp2_fast(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        m = m_new;
+      }
+      float lt = 0.f;
+      u32x4 pw0[2], pw1[2];
+      // B: S(j+1), keys 32..63, beside the softmax of tile j's keys 0..31.
+      s_half(sn, buf ^ 1, 1);
+      softmax_half(sc, 0, lt, pw0);
+      // C: O(j), keys 0..31, beside the softmax of keys 32..63.
+      o_half(buf, 0, pw0);
+      softmax_half(sc, 1, lt, pw1);
+      // D: O(j), keys 32..63.
+      o_half(buf, 1, pw1);
+      l += lt + __shfl_xor(lt, 32);
+    }
+    if (j + 2 < ntiles) store_k(buf);
+    if (j + 1 < ntiles) store_v(buf ^ 1);
+    __syncthreads();
+  };
+
+  // Prologue: K(0), V(0) and K(1) into LDS, then S^T of tile 0.
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  if (ntiles > 1) {
+    load_k(FA_BKV);
+    store_k(1);
+  }
+  __syncthreads();
+  f32x16 sA[2], sB[2];
+  s_half(sA, 0, 0);
+  s_half(sA, 0, 1);
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(j, sA, sB);
+    if (j + 1 < ntiles) tile(j + 1, sB, sA);
+  }
+
+  // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4.
+  if (my_q < T) {
+    const float inv = 1.0f / l;
+    uint16_t* op = o + static_cast<int64_t>(my_q) * ld_q + h * FA_D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) op[db * 32 + 8 * (e >> 2) + 4 * half + (e & 3)] = f32_to_bf16(oacc[db][e] * inv);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
@@ -359,8 +590,8 @@ bool flash_attn_supported(int dh) { return dh == FA_D; }
 hipError_t launch_flash_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
                              int H, int G, int dh, hipStream_t stream) {
   const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(dh)));
-  const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + FA_BQ - 1) / FA_BQ));
-  flash_attn_fwd_kernel<<<grid, FA_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
+  const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + F2_BQ - 1) / F2_BQ));
+  flash_attn_fwd2_kernel<<<grid, F2_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
   return hipGetLastError();
 }
 
