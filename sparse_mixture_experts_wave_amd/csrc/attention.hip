@@ -131,207 +131,18 @@ __global__ void row_range_kernel(int32_t* __restrict__ offsets, int32_t rows) {
 // ---------------------------------------------------------------------------
 // causal GQA flash attention, d_h = 128
 // ---------------------------------------------------------------------------
-constexpr int FA_D = 128;                // head dimension
-constexpr int FA_BQ = 128;               // queries per workgroup (4 waves x 32)
-constexpr int FA_BKV = 64;               // keys per tile
-constexpr int FA_NT = 256;
-constexpr int VT_STRIDE = FA_BKV + 4;    // 68 bf16 = 136 bytes per transposed V row
-
-__device__ __forceinline__ int kswz(int key, int chunk) { return key * FA_D + ((chunk ^ (key & 15)) << 3); }
-
-__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
-
-// 2^x with the hardware instruction alone (v_exp_f32): results below 2^-126
-// flush to zero instead of being rebuilt as denormals, which a softmax weight
-// that small never needs (exp2f would spend about six instructions on it).
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ k,
-                                                               const uint16_t* __restrict__ v,
-                                                               uint16_t* __restrict__ o, int T, int H, int G,
-                                                               float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[FA_BKV * FA_D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[FA_D * VT_STRIDE];
-
-  const int h = blockIdx.x;                                   // heads of a K/V group are adjacent
-  const int n_qt = (T + FA_BQ - 1) / FA_BQ;
-  const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * FA_BQ;  // longest rows first
-  const int g = h / (H / G);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int half = lane >> 5;
-  const int qw = q0 + wave * 32;         // first query of the wave
-  const int my_q = qw + (lane & 31);     // the lane's query: its column of S^T and O^T
-  const int64_t ld_q = static_cast<int64_t>(H) * FA_D;
-  const int64_t ld_kv = static_cast<int64_t>(G) * FA_D;
-
-  // B operand of S^T = K Q^T: lane holds query my_q, dims 16 ks + 8 half .. +7.
-  bf16x8 qf[8];
-  {
-    const uint16_t* qp = q + static_cast<int64_t>(min(my_q, T - 1)) * ld_q + h * FA_D + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(load16(qp + 16 * ks));
-  }
-  f32x16 oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const int kv_end = min(T, q0 + FA_BQ);
-  // Tile t+1 is loaded into registers while tile t is computed from LDS, and
-  // stored to LDS between two barriers once every wave is done with tile t.
-  // K: 4 x 16-byte chunks of rows key = c / 16 (c = 4 tid + i); V: keys
-  // 4 kg .. 4 kg + 3 x dims 8 dg .. 8 dg + 7, stored transposed.  Keys past T
-  // are clamped to T-1: they lie above every query, so the mask removes them.
-  const int kg = tid & 15, dg = tid >> 4;
-  u32x4 kr[4], vr[4];
-  auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid * 4 + i;
-      const int kk = min(kv0 + (c >> 4), T - 1);
-      kr[i] = load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + (c & 15) * 8);
-      vr[i] = load16(v + static_cast<int64_t>(min(kv0 + 4 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid * 4 + i;
-      store16(Ks + kswz(c >> 4, c & 15), kr[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t e[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e[i] = (j & 1) ? hi16(vr[i][j >> 1]) : lo16(vr[i][j >> 1]);
-      uint2 packed;
-      packed.x = e[0] | (e[1] << 16);
-      packed.y = e[2] | (e[3] << 16);
-      *reinterpret_cast<uint2*>(Vt + (8 * dg + j) * VT_STRIDE + 4 * kg) = packed;
-    }
-  };
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-  for (int kv0 = 0; kv0 < kv_end; kv0 += FA_BKV) {
-    const bool more = kv0 + FA_BKV < kv_end;
-    if (more) load_tile(kv0 + FA_BKV);
-
-    if (kv0 <= qw + 31) {  // some key of the tile is visible to some query of the wave
-      // S^T: rows = keys kv0 + 32 kb + 8 (e / 4) + 4 half + e % 4, column = my_q.
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 a = as_bf16x8(load16(Ks + kswz(kb * 32 + (lane & 31), 2 * ks + half)));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-        }
-      }
-      // Causal mask, only on tiles that reach past the wave's first query.
-      if (kv0 + FA_BKV - 1 > qw) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kv0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3) > my_q) s[kb][e] = -INFINITY;
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, s[kb][e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;  // the tile's max, in log2 units
-      // Lazy rescaling: the reference max m only moves when the tile's max
-      // exceeds it by more than 8, so every p = 2^(s - m) stays <= 2^8 and the
-      // rescale of O and l is skipped on most tiles.  O / l does not depend on
-      // m.  m is finite after the first tile: key 0 is visible to every query.
-      if (__ballot(mt > m + 8.f)) {
-        const float m_new = mt > m + 8.f ? mt : m;
-        const float alpha = exp2_fast(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        m = m_new;
-      }
-      float lt = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2_fast(fmaf(s[kb][e], scale_log2, -m));
-          s[kb][e] = p;
-          lt += p;
-        }
-      lt += __shfl_xor(lt, 32);
-      l += lt;
-      // O^T += V^T P^T over four 16-key steps.  Step j takes accumulator
-      // entries e = 8 (j & 1) .. +7 of block j >> 1: for lane half q these are
-      // keys base + 0..3 and base + 8..11 with base = 32 (j>>1) + 16 (j&1) + 4q,
-      // and the A operand reads V^T at exactly those keys.
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kb = j >> 1, hf = j & 1;
-        u32x4 pw;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) pw[t] = cvt_pk_bf16(s[kb][8 * hf + 2 * t], s[kb][8 * hf + 2 * t + 1]);
-        const bf16x8 pb = as_bf16x8(pw);
-        const int base = kb * 32 + hf * 16 + 4 * half;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint16_t* vr = Vt + (db * 32 + (lane & 31)) * VT_STRIDE + base;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-          u32x4 aw;
-          aw[0] = lo.x;
-          aw[1] = lo.y;
-          aw[2] = hi.x;
-          aw[3] = hi.y;
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aw), pb, oacc[db], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
-    if (more) {
-      store_tile();
-      __syncthreads();
-    }
-  }
-
-  // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4.
-  if (my_q < T) {
-    const float inv = 1.0f / l;
-    uint16_t* op = o + static_cast<int64_t>(my_q) * ld_q + h * FA_D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) op[db * 32 + 8 * (e >> 2) + 4 * half + (e & 3)] = f32_to_bf16(oacc[db][e] * inv);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// causal GQA flash attention, software-pipelined per wave
-// ---------------------------------------------------------------------------
-// Eight waves (two per SIMD) of 32 queries each share 64-key K / V tiles.  Per
-// tile j a wave runs, in order:
+// A workgroup takes 256 queries of one head: eight waves (two per SIMD) of 32
+// queries, walking 64-key tiles up to the diagonal.  Each wave computes
+// S^T = K Q^T so that a lane's accumulator column is one query: the running
+// max, the exponentials and the running sum stay in the lane (one exchange
+// with the lane 32 apart per tile), and P^T feeds O^T = V^T P^T as the B
+// operand straight from registers, the MFMA's k order taken to be the order in
+// which the S^T accumulator holds the keys; V is staged transposed in LDS.
+// The softmax is rescaled lazily: the reference max moves only when a tile's
+// max exceeds it by more than 8 (log2 units).  Heads of one K/V group are
+// adjacent in the grid, the longest query tiles first.
+//
+// Software pipelining.  Per tile j a wave runs, in order:
 //   A: S(j+1) for keys 0..31 of tile j+1 (8 MFMAs) beside tile j's row max;
 //   (the lazy-rescale branch, rarely taken);
 //   B: S(j+1) for keys 32..63 beside exp / sum / bf16 packing of tile j's
@@ -342,33 +153,53 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 // V^T have two LDS buffers each: while tile j is consumed, K(j+2) goes into the
 // buffer K(j) used and V(j+1) into the buffer V(j-1) used, so one barrier per
 // tile suffices.
-constexpr int F2_NW = 8;                   // waves per workgroup
-constexpr int F2_QW = 32;                  // queries per wave
-constexpr int F2_BQ = F2_QW * F2_NW;       // queries per workgroup
-constexpr int F2_NT = 64 * F2_NW;
-constexpr int F2_LD = FA_D + 8;            // padded K / Q row: 272 bytes
-constexpr int F2_KC = FA_BKV * FA_D / 8 / F2_NT;  // 16-byte K chunks per thread per tile (2)
+constexpr int FA_D = 128;                // head dimension
+constexpr int FA_BKV = 64;               // keys per tile
+constexpr int VT_STRIDE = FA_BKV + 4;    // 68 bf16 = 136 bytes per transposed V row
+
+__device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// 2^x with the hardware instruction alone (v_exp_f32): results below 2^-126
+// flush to zero instead of being rebuilt as denormals, which a softmax weight
+// that small never needs (exp2f would spend about six instructions on it).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr int FA_NW = 8;                   // waves per workgroup
+constexpr int FA_QW = 32;                  // queries per wave
+constexpr int FA_BQ = FA_QW * FA_NW;       // queries per workgroup
+constexpr int FA_NT = 64 * FA_NW;
+constexpr int FA_LD = FA_D + 8;            // padded K row: 272 bytes
+constexpr int FA_KC = FA_BKV * FA_D / 8 / FA_NT;  // 16-byte K chunks per thread per tile (2)
 
 // K rows padded to 272 bytes: the 16 rows one operand read touches start
 // 4 banks apart (conflict-free), and every chunk of a lane's row is a constant
 // offset from one address.
-__device__ __forceinline__ int kpad(int row, int chunk) { return row * F2_LD + chunk * 8; }
+__device__ __forceinline__ int kpad(int row, int chunk) { return row * FA_LD + chunk * 8; }
 
-__global__ __launch_bounds__(F2_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd2_kernel(
+__global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, int T, int H, int G, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BKV * F2_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BKV * FA_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][FA_D * VT_STRIDE];
 
   const int h = blockIdx.x;
-  const int n_qt = (T + F2_BQ - 1) / F2_BQ;
-  const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * F2_BQ;  // longest rows first
+  const int n_qt = (T + FA_BQ - 1) / FA_BQ;
+  const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * FA_BQ;  // longest rows first
   const int g = h / (H / G);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
-  const int qw = q0 + wave * F2_QW;        // first query of the wave
+  const int qw = q0 + wave * FA_QW;        // first query of the wave
   const int my_q = qw + (lane & 31);       // the lane's query: its column of S^T and O^T
   const int64_t ld_q = static_cast<int64_t>(H) * FA_D;
   const int64_t ld_kv = static_cast<int64_t>(G) * FA_D;
@@ -388,18 +219,18 @@ __global__ __launch_bounds__(F2_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int kv_end = min(T, q0 + F2_BQ);
+  const int kv_end = min(T, q0 + FA_BQ);
   const int ntiles = (kv_end + FA_BKV - 1) / FA_BKV;
   // K/V staging through registers.  K: chunks c = KC tid + i, row c / 16.
   // V: keys 2 kg, 2 kg + 1 (kg = tid % 32) x dims 8 dg .. 8 dg + 7
   // (dg = tid / 32), stored transposed.  Keys past T are clamped to T - 1:
   // they lie above every query, so the mask removes them.
   const int kg = tid & 31, dg = tid >> 5;
-  u32x4 kr[F2_KC], vr[2];
+  u32x4 kr[FA_KC], vr[2];
   auto load_k = [&](int kv0) {
 #pragma unroll
-    for (int i = 0; i < F2_KC; ++i) {
-      const int c = tid * F2_KC + i;
+    for (int i = 0; i < FA_KC; ++i) {
+      const int c = tid * FA_KC + i;
       const int kk = min(kv0 + (c >> 4), T - 1);
       kr[i] = load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + (c & 15) * 8);
     }
@@ -411,8 +242,8 @@ __global__ __launch_bounds__(F2_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
   auto store_k = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < F2_KC; ++i) {
-      const int c = tid * F2_KC + i;
+    for (int i = 0; i < FA_KC; ++i) {
+      const int c = tid * FA_KC + i;
       store16(&Ks[buf][kpad(c >> 4, c & 15)], kr[i]);
     }
   };
@@ -482,7 +313,7 @@ __global__ __launch_bounds__(F2_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int buf = j & 1;
     if (j + 2 < ntiles) load_k(kv0 + 2 * FA_BKV);
     if (j + 1 < ntiles) load_v(kv0 + FA_BKV);
-    if (kv0 <= qw + F2_QW - 1) {  // some key of tile j is visible to some query of the wave
+    if (kv0 <= qw + FA_QW - 1) {  // some key of tile j is visible to some query of the wave
       if (kv0 + FA_BKV - 1 > qw) {  // causal mask on the diagonal tiles only
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -590,8 +421,8 @@ bool flash_attn_supported(int dh) { return dh == FA_D; }
 hipError_t launch_flash_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
                              int H, int G, int dh, hipStream_t stream) {
   const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(dh)));
-  const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + F2_BQ - 1) / F2_BQ));
-  flash_attn_fwd2_kernel<<<grid, F2_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
+  const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + FA_BQ - 1) / FA_BQ));
+  flash_attn_fwd_kernel<<<grid, FA_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
   return hipGetLastError();
 }
 
