@@ -14,17 +14,18 @@
 // turns HF's half-split rotation into the interleaved one.  So pair
 // (2i, 2i+1) of a head vector at position p turns by p * theta^(-2i/d_h).
 //
-// Flash attention.  A 256-thread workgroup owns 128 queries of one head (32
-// per wave) and walks the key axis in 64-key tiles up to the diagonal.  Each
-// wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so that a lane's
-// accumulator column is one query: the running max, the exponentials and the
-// running sum of a query stay in its lane and the lane 32 apart (one
-// cross-lane exchange per tile).  P^T then feeds O^T = V^T P^T straight from
-// registers as the B operand: the k-index order of the MFMA is taken to be the
-// order in which the S^T accumulator holds the keys, and V^T is read from LDS
-// in that same order.  K is staged in LDS as [key][d_h] with 16-byte chunks
-// XOR-swizzled by key; V is staged transposed, [d_h][key], in 136-byte rows so
-// the 32 head dimensions an operand read touches fall in distinct banks.
+// Flash attention.  A 512-thread workgroup owns 256 queries of one head (32
+// per wave, two waves per SIMD) and walks the key axis in 64-key tiles up to
+// the diagonal.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
+// so that a lane's accumulator column is one query: the running max, the
+// exponentials and the running sum of a query stay in its lane and the lane 32
+// apart (one cross-lane exchange per tile).  P^T then feeds O^T = V^T P^T
+// straight from registers as the B operand: the k-index order of the MFMA is
+// taken to be the order in which the S^T accumulator holds the keys, and V^T
+// is read from LDS in that same order.  K is staged in LDS as [key][d_h] in
+// 272-byte rows, V transposed, [d_h][key], in 136-byte rows, so the operand
+// reads of both are free of bank conflicts.  The next tile's S MFMAs are
+// interleaved with the current tile's softmax (see the kernel below).
 #include "device_common.h"
 #include "kernels.h"
 
