@@ -23,8 +23,9 @@
 // straight from registers as the B operand: the k-index order of the MFMA is
 // taken to be the order in which the S^T accumulator holds the keys, and V^T
 // is read from LDS in that same order.  K is staged in LDS as [key][d_h] in
-// 272-byte rows, V transposed, [d_h][key], in 136-byte rows, so the operand
-// reads of both are free of bank conflicts.  The next tile's S MFMAs are
+// 272-byte rows, V transposed, [d_h][key], in 144-byte rows with the keys of
+// each 16-key group reordered so that every operand is one 16-byte read; the
+// operand reads of both are free of bank conflicts.  The next tile's S MFMAs are
 // interleaved with the current tile's softmax (see the kernel below).
 #include "device_common.h"
 #include "kernels.h"
@@ -156,7 +157,7 @@ __global__ void row_range_kernel(int32_t* __restrict__ offsets, int32_t rows) {
 // tile suffices.
 constexpr int FA_D = 128;                // head dimension
 constexpr int FA_BKV = 64;               // keys per tile
-constexpr int VT_STRIDE = FA_BKV + 4;    // 68 bf16 = 136 bytes per transposed V row
+constexpr int VT_STRIDE = FA_BKV + 8;    // 72 bf16 = 144 bytes per transposed V row
 
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
@@ -174,6 +175,8 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // that small never needs (exp2f would spend about six instructions on it).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr bf16x2 kOnesBf16x2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
 constexpr int FA_NW = 8;                   // waves per workgroup
 constexpr int FA_QW = 32;                  // queries per wave
 constexpr int FA_BQ = FA_QW * FA_NW;       // queries per workgroup
@@ -185,6 +188,17 @@ constexpr int FA_KC = FA_BKV * FA_D / 8 / FA_NT;  // 16-byte K chunks per thread
 // 4 banks apart (conflict-free), and every chunk of a lane's row is a constant
 // offset from one address.
 __device__ __forceinline__ int kpad(int row, int chunk) { return row * FA_LD + chunk * 8; }
+
+// Column of key kk (0..63) in a transposed V row.  Within each 16-key group
+// the keys are reordered so that the eight keys one lane feeds to an MFMA
+// step (4 q + 0..3 and 8 + 4 q + 0..3 for lane half q) are adjacent: key
+// 4 q + 8 h + i of the group goes to column 8 q + 4 h + i.  Rows of 144 bytes
+// keep the 16-byte operand reads aligned and the 16 rows of one read in
+// distinct banks.
+__device__ __forceinline__ int vt_col(int kk) {
+  const int r = kk & 15;
+  return (kk & ~15) + 8 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
 
 __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void flash_attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -222,24 +236,28 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   const int kv_end = min(T, q0 + FA_BQ);
   const int ntiles = (kv_end + FA_BKV - 1) / FA_BKV;
-  // K/V staging through registers.  K: chunks c = KC tid + i, row c / 16.
-  // V: keys 2 kg, 2 kg + 1 (kg = tid % 32) x dims 8 dg .. 8 dg + 7
-  // (dg = tid / 32), stored transposed.  Keys past T are clamped to T - 1:
-  // they lie above every query, so the mask removes them.
+  // K/V staging through registers.  K: 16-byte chunks c = 2 tid, 2 tid + 1,
+  // both of row tid / 8.  V: keys 2 kg, 2 kg + 1 (kg = tid % 32) x dims
+  // 8 dg .. 8 dg + 7 (dg = tid / 32), stored transposed, the two keys side by
+  // side at column vt_col(2 kg).  Keys past T are clamped to T - 1: they lie
+  // above every query, so the mask removes them.  Row offsets are 32-bit
+  // (24-bit multiplies): the launcher rejects T * G * d_h >= 2^31.
+  static_assert(FA_KC == 2, "two K chunks per thread");
   const int kg = tid & 31, dg = tid >> 5;
+  const uint32_t ld_kv32 = static_cast<uint32_t>(ld_kv);
+  const uint16_t* kbase = k + g * FA_D + ((FA_KC * tid) & 15) * 8;
+  const uint16_t* vbase = v + g * FA_D + 8 * dg;
+  const int vcol = vt_col(2 * kg);
   u32x4 kr[FA_KC], vr[2];
   auto load_k = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < FA_KC; ++i) {
-      const int c = tid * FA_KC + i;
-      const int kk = min(kv0 + (c >> 4), T - 1);
-      kr[i] = load16(k + static_cast<int64_t>(kk) * ld_kv + g * FA_D + (c & 15) * 8);
-    }
+    const uint32_t ro = __umul24(static_cast<uint32_t>(min(kv0 + (tid >> 3), T - 1)), ld_kv32);
+    kr[0] = load16(kbase + ro);
+    kr[1] = load16(kbase + ro + 8);
   };
   auto load_v = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      vr[i] = load16(v + static_cast<int64_t>(min(kv0 + 2 * kg + i, T - 1)) * ld_kv + g * FA_D + 8 * dg);
+      vr[i] = load16(vbase + __umul24(static_cast<uint32_t>(min(kv0 + 2 * kg + i, T - 1)), ld_kv32));
   };
   auto store_k = [&](int buf) {
 #pragma unroll
@@ -253,7 +271,7 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     for (int j = 0; j < 8; ++j) {
       const uint32_t e0 = (j & 1) ? hi16(vr[0][j >> 1]) : lo16(vr[0][j >> 1]);
       const uint32_t e1 = (j & 1) ? hi16(vr[1][j >> 1]) : lo16(vr[1][j >> 1]);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dg + j) * VT_STRIDE + 2 * kg]) = e0 | (e1 << 16);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dg + j) * VT_STRIDE + vcol]) = e0 | (e1 << 16);
     }
   };
   // S^T of keys 32 kb .. 32 kb + 31 of the tile in buffer buf: rows = keys
@@ -277,30 +295,27 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const int e = 8 * hf + 2 * t;
         const float p0 = exp2_fast(fmaf(s[kb][e], scale_log2, -m));
         const float p1 = exp2_fast(fmaf(s[kb][e + 1], scale_log2, -m));
-        lt += p0 + p1;
-        pw[hf][t] = cvt_pk_bf16(p0, p1);
+        // The row sum adds the bf16 weights the O MFMAs use: v_dot2 with
+        // (1, 1), one instruction per pair.  (The packed word is copied to a
+        // scalar first: a bit cast of an element of a vector variable reads
+        // the wrong element with this compiler.)
+        const uint32_t pp = cvt_pk_bf16(p0, p1);
+        pw[hf][t] = pp;
+        lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp), kOnesBf16x2, lt, false);
       }
   };
   // O^T += V^T P^T over the two 16-key steps of keys 32 kb .. + 31.  Step hf
   // takes accumulator entries e = 8 hf .. +7, i.e. for lane half q the keys
-  // base + 0..3 and base + 8..11 with base = 32 kb + 16 hf + 4 q, and the A
-  // operand reads V^T at exactly those keys.
+  // 16 g + 4 q + 0..3 and 16 g + 8 + 4 q + 0..3 of 16-key group g = 2 kb + hf,
+  // which V^T holds in that order at columns 16 g + 8 q .. + 7: one 16-byte
+  // operand read each.
   auto o_half = [&](int buf, int kb, const u32x4 (&pw)[2]) {
     u32x4 aw[2][4];  // all operand reads first
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int base = kb * 32 + hf * 16 + 4 * half;
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint16_t* vp = &Vt[buf][(db * 32 + (lane & 31)) * VT_STRIDE + base];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-        aw[hf][db][0] = lo.x;
-        aw[hf][db][1] = lo.y;
-        aw[hf][db][2] = hi.x;
-        aw[hf][db][3] = hi.y;
-      }
-    }
+      for (int db = 0; db < 4; ++db)
+        aw[hf][db] = load16(&Vt[buf][(db * 32 + (lane & 31)) * VT_STRIDE + 16 * (2 * kb + hf) + 8 * half]);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -421,6 +436,7 @@ bool flash_attn_supported(int dh) { return dh == FA_D; }
 
 hipError_t launch_flash_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
                              int H, int G, int dh, hipStream_t stream) {
+  if (T * G * static_cast<int64_t>(dh) >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(dh)));
   const dim3 grid(static_cast<unsigned>(H), static_cast<unsigned>((T + FA_BQ - 1) / FA_BQ));
   flash_attn_fwd_kernel<<<grid, FA_NT, 0, stream>>>(q, k, v, o, static_cast<int>(T), H, G, scale_log2);
