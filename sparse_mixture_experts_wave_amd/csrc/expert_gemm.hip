@@ -96,6 +96,20 @@ __device__ __forceinline__ void bar() {
   asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
+// The barriers that only one wave group executes (the half-step offset) carry
+// asm text of their own: the optimiser never executes a volatile asm on a
+// path where it was not, but it may merge identical ones, and merging one of
+// these with a barrier both groups run would change the barrier counts.
+__device__ __forceinline__ void bar_group1_start() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier  ; group 1 starts one interval late" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void bar_group0_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier  ; group 0 ends one interval late" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct Tile {
   int e, m0, rows, n0;
@@ -281,7 +295,7 @@ __device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32
   else
     wait_vmcnt<0>();
   bar();
-  if (grp == 1) bar();  // group 1 starts one interval late
+  if (grp == 1) bar_group1_start();
   int s = 0;
   for (; s + NS <= KT; s += NS) {
     slice_step<GATED, FULL, 0>(cs, s, KT, grp, live, acc);
@@ -294,7 +308,7 @@ __device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32
   if (s + 1 < KT) slice_step<GATED, FULL, 1>(cs, s + 1, KT, grp, live, acc);
   if (s + 2 < KT) slice_step<GATED, FULL, 2>(cs, s + 2, KT, grp, live, acc);
   if (s + 3 < KT) slice_step<GATED, FULL, 3>(cs, s + 3, KT, grp, live, acc);
-  if (grp == 0) bar();  // ... and group 0 ends one interval late: same barrier count
+  if (grp == 0) bar_group0_end();  // same barrier count for both groups
 }
 
 // Number of tiles (sum over experts of the row tiles, times NT).
