@@ -41,6 +41,29 @@ def test_gqa_attention_core(T, H, G):
     assert np.array_equal(got[0], np.repeat(v0, r, axis=0))
 
 
+def test_gqa_attention_mixtral_t4096_sampled():
+    """The benchmarked core: T = 4096, 32 query heads, 8 K/V groups, d_h = 128,
+    the heads bench.py times (attention_heads, default seed), one launch as
+    bench.py makes it.  Sampled queries (both sides of query-tile and key-tile
+    boundaries, the last query, random ones) against the oracle one query at a
+    time: query t is the last of t + 1 positions and sees keys 0..t."""
+    T, H, G = 4096, 32, 8
+    say(f"gqa core sampled T={T} H={H} G={G}")
+    inp = attention_heads(T, H, G, 128)
+    o = moe.moe_gqa_attention(to_dev(inp["q"]), to_dev(inp["k"]), to_dev(inp["v"]))
+    torch.cuda.synchronize()
+    got = widen_host(to_host(o))
+    rng = np.random.default_rng(11)
+    ts = sorted({0, 1, 31, 32, 63, 64, 255, 256, 257, 2047, 2048, 3839, 3840, 4094, 4095,
+                 *rng.integers(0, T, 17).tolist()})
+    refs = [oracle.gqa_attention_ref(inp["q"][t:t + 1], inp["k"][:t + 1], inp["v"][:t + 1], causal=True)[0]
+            for t in ts]
+    scale = max(float(np.max(np.abs(r))) for r in refs)
+    for t, ref in zip(ts, refs):
+        err = float(np.max(np.abs(got[t] - ref)))
+        assert err <= BF16_TOL * scale, (t, err)
+
+
 def test_gqa_attention_is_deterministic_and_causal():
     say("gqa determinism / causality")
     T, H, G = 500, 8, 2
