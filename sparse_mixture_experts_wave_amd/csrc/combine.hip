@@ -12,31 +12,46 @@
 namespace moe {
 namespace {
 
-template <bool OUT_BF16>
+// K = top-k, a template parameter so that a thread loads every slot's row
+// index and weight first and then has all 2K row loads in flight; the sums
+// still run in slot order.  Indices are 32-bit: the entry points keep
+// T * d below 2^31.
+template <bool OUT_BF16, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ inv_pos,
                                                       const float* __restrict__ topk_w,
-                                                      const void* residual, void* y, int64_t T,
-                                                      int k, int d) {
+                                                      const void* residual, void* y, int T, int d) {
   const int groups_per_row = d >> 3;
-  const int64_t total = T * groups_per_row;
-  for (int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; g < total;
-       g += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t t = g / groups_per_row;
-    const int col = static_cast<int>(g - t * groups_per_row) * 8;
+  const int total = T * groups_per_row;
+  for (int g = blockIdx.x * blockDim.x + threadIdx.x; g < total; g += gridDim.x * blockDim.x) {
+    const int t = g / groups_per_row;
+    const int col = (g - t * groups_per_row) * 8;
+    int row[K];
+    float w[K];
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      row[s] = inv_pos[t * K + s];
+      w[s] = topk_w[t * K + s];
+    }
+    float4 a[K], b[K];
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      if (row[s] >= 0) {
+        const float4* src = reinterpret_cast<const float4*>(y_sorted + static_cast<int64_t>(row[s]) * d + col);
+        a[s] = src[0];
+        b[s] = src[1];
+      }
+    }
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int s = 0; s < k; ++s) {
-      const int row = inv_pos[t * k + s];
-      if (row < 0) continue;
-      const float w = topk_w[t * k + s];
-      const float4* src = reinterpret_cast<const float4*>(y_sorted + static_cast<int64_t>(row) * d + col);
-      const float4 a = src[0], b = src[1];
-      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+#pragma unroll
+    for (int s = 0; s < K; ++s) {
+      if (row[s] < 0) continue;
+      acc[0] += w[s] * a[s].x; acc[1] += w[s] * a[s].y; acc[2] += w[s] * a[s].z; acc[3] += w[s] * a[s].w;
+      acc[4] += w[s] * b[s].x; acc[5] += w[s] * b[s].y; acc[6] += w[s] * b[s].z; acc[7] += w[s] * b[s].w;
     }
-    const int64_t off = t * d + col;
+    const int64_t off = static_cast<int64_t>(t) * d + col;
     if constexpr (OUT_BF16) {
       if (residual != nullptr) {
         const u32x4 r = load16(static_cast<const uint16_t*>(residual) + off);
@@ -53,9 +68,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     } else {
       if (residual != nullptr) {
         const float4* r = reinterpret_cast<const float4*>(static_cast<const float*>(residual) + off);
-        const float4 a = r[0], b = r[1];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+        const float4 ra = r[0], rb = r[1];
+        acc[0] += ra.x; acc[1] += ra.y; acc[2] += ra.z; acc[3] += ra.w;
+        acc[4] += rb.x; acc[5] += rb.y; acc[6] += rb.z; acc[7] += rb.w;
       }
       float4* o = reinterpret_cast<float4*>(static_cast<float*>(y) + off);
       o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -64,19 +79,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+template <bool OUT_BF16>
+hipError_t launch_k(const float* y_sorted, const int32_t* inv_pos, const float* topk_w, const void* residual,
+                    void* y, int T, int k, int d, unsigned blocks, hipStream_t s) {
+#define MOE_COMBINE_K(KK)                                                                                  \
+  case KK:                                                                                                \
+    combine_kernel<OUT_BF16, KK><<<blocks, 256, 0, s>>>(y_sorted, inv_pos, topk_w, residual, y, T, d); \
+    break;
+  switch (k) {
+    MOE_COMBINE_K(1)
+    MOE_COMBINE_K(2)
+    MOE_COMBINE_K(3)
+    MOE_COMBINE_K(4)
+    MOE_COMBINE_K(5)
+    MOE_COMBINE_K(6)
+    MOE_COMBINE_K(7)
+    MOE_COMBINE_K(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MOE_COMBINE_K
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const float* y_sorted, const int32_t* inv_pos, const float* topk_w,
                           const void* residual, void* y, bool out_bf16, int64_t T, int k, int d,
                           hipStream_t stream) {
+  if (T * d >= (int64_t{1} << 31)) return hipErrorInvalidValue;
   const int64_t groups = T * (d / 8);
   int64_t blocks = (groups + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (out_bf16)
-    combine_kernel<true><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(y_sorted, inv_pos, topk_w, residual, y, T, k, d);
-  else
-    combine_kernel<false><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(y_sorted, inv_pos, topk_w, residual, y, T, k, d);
-  return hipGetLastError();
+  const unsigned nb = static_cast<unsigned>(blocks);
+  const int Ti = static_cast<int>(T);
+  return out_bf16 ? launch_k<true>(y_sorted, inv_pos, topk_w, residual, y, Ti, k, d, nb, stream)
+                  : launch_k<false>(y_sorted, inv_pos, topk_w, residual, y, Ti, k, d, nb, stream);
 }
 
 }  // namespace moe
