@@ -279,11 +279,14 @@ def test_forward_is_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_block_forward_two_layers_teacher_forced():
-    cfg = small("block", 300, 256, 384)
+@pytest.mark.parametrize("T", [300, 701])
+def test_block_forward_two_layers_teacher_forced(T):
+    """T = 300 routes one token per workgroup, T = 701 four (the last one
+    ragged), both with the RMSNorm fused into the router."""
+    cfg = small("block", T, 256, 384)
     dv_h = None
     for layer in range(2):
-        say(f"block layer {layer}")
+        say(f"block T={T} layer {layer}")
         inp = generate(cfg, layer=layer)
         if dv_h is None:
             dv_h = to_dev(inp["x"])
