@@ -47,6 +47,8 @@ def run_forward(inp):
     (65, 256, 32, "f32", None),
     (33, 256, 64, "bf16", None),
     (1, 4096, 8, "bf16", None),
+    (4097, 512, 8, "bf16", None),           # two tokens per wave group, the last ragged
+    (8195, 256, 8, "bf16", "zipf1.2"),      # four tokens per wave group, the last ragged
 ])
 def test_router_parity(T, d, E, dtype, bias):
     say(f"router T={T} d={d} E={E} {dtype} bias={bias}")
