@@ -13,7 +13,9 @@ HBM-bound); the prefill layer (T = 4096), the Zipf-skewed layer (T = 16384)
 and the 32-layer residual stack (T = 2048, one step = all 32 sublayers) are
 measured too and reported under "secondary"; the small-T decode latency
 sweep under "decode_latency"; the attention sublayer around the MoE (GQA with
-RoPE at Mixtral widths, T = 4096) and a whole decoder layer under "attention".  Per-kernel durations come from HIP events that
+RoPE at Mixtral widths, T = 4096) and a whole decoder layer under "attention";
+one expert-parallel rank's share of the prefill layer (one local expert, 1024
+rows, full width) under "ep_rank".  Per-kernel durations come from HIP events that
 moe_forward records on its own stream between its kernels (timing points of
 the C ABI); the roofline fraction is that of the dominant kernel.
 """
@@ -307,6 +309,40 @@ def measure_decode_latency(steps: int, Ts=(1, 2, 4, 8, 16)):
     return out
 
 
+def measure_ep_rank(steps: int, rows: int = 1024):
+    """One expert-parallel rank's share of the prefill layer at full width.
+    With expert e on GPU e, T = 4096 and top-2, a rank holds one expert and
+    receives about 2T/8 = 1024 rows; its work is the grouped-GEMM expert FFN
+    (up with the SiLU*gate epilogue, then down) on those rows.  Every row is
+    routed to local expert 0; the layout carries a second, empty expert because
+    the entry points take E >= 2."""
+    import torch
+
+    import sparse_mixture_experts_wave_amd as moe
+    from synth import CONFIGS, generate_torch
+
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS["mixtral_prefill_t4096"].with_(name="ep_rank_t4096", T=rows, E=2, k=1)
+    dv = generate_torch(cfg, dev)
+    off = torch.tensor([0, rows, rows], dtype=torch.int32, device=dev)
+    st = torch.arange(rows, dtype=torch.int32, device=dev)
+    y = torch.empty((rows, cfg.d), dtype=torch.float32, device=dev)
+    args = (dv["x"], off, st, dv["w1"], dv["w3"], dv["w2"])
+    for _ in range(3):
+        moe.moe_expert_ffn(*args, k=1, y_sorted=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        moe.moe_expert_ffn(*args, k=1, y_sorted=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 6.0 * rows * cfg.d * cfg.d_ff / (ms * 1e-3) / 1e12
+    return {"workload": "ep_rank_t4096", "rows": rows, "d": cfg.d, "d_ff": cfg.d_ff, "local_experts": 1,
+            "ms": round(ms, 4), "tflops": round(tflops, 1), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: int = 8, dh: int = 128,
                       theta: float = 1e6):
     """The attention sublayer around the MoE at Mixtral 8x7B widths (32 query
@@ -463,6 +499,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-latency", action="store_true", help="skip the small-T decode latency sweep")
     ap.add_argument("--no-attention", action="store_true", help="skip the attention sublayer workload")
+    ap.add_argument("--no-ep-rank", action="store_true", help="skip the expert-parallel rank workload")
     ap.add_argument("--attention-only", action="store_true",
                     help="measure only the attention sublayer workload and print its JSON")
     ap.add_argument("--cpu-tokens", type=int, default=16)
@@ -523,6 +560,11 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] attention sublayer", file=sys.stderr, flush=True)
         attention = measure_attention(max(3, a.steps // 2))
+    ep_rank = None
+    if not a.no_ep_rank:
+        torch.cuda.empty_cache()
+        print("[bench] expert-parallel rank share", file=sys.stderr, flush=True)
+        ep_rank = measure_ep_rank(max(5, a.steps))
     out = {
         "metric": METRIC, "value": prim["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": prim["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -530,7 +572,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "d_ff": cfg.d_ff, "E": cfg.E, "k": cfg.k,
                    "parallelism": "single GPU"},
         "roofline": prim["roofline"], "cpu_baseline": cpu, "detail": prim, "secondary": sec,
-        "decode_latency": latency, "attention": attention,
+        "decode_latency": latency, "attention": attention, "ep_rank": ep_rank,
     }
     print(json.dumps(out), flush=True)
 

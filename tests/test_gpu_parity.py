@@ -193,6 +193,7 @@ def test_expert_ffn(T, d, d_ff, dtype, path):
     (512, 1024, [1024, 1024]),         # up 64 tiles in 4 K pieces, down 16 tiles in 8
     (1024, 2048, [300, 257, 1, 700]),  # ragged experts: up 128 tiles in 2 pieces, down 32 tiles in 8
     (512, 4096, [1500, 1100]),         # up 352 tiles: 256 whole, 96 in 2 pieces; down 22 tiles in 8
+    (512, 1024, [1024, 0]),            # one expert-parallel rank: every row on one local expert
 ])
 def test_expert_ffn_split_last_round(d, d_ff, counts):
     """The grouped GEMM splits the tiles of its last round along K (on a
