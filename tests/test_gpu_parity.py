@@ -114,6 +114,23 @@ def test_dispatch_bit_exact(T, E, mode):
     assert np.array_equal(to_host(inv), inv_ref)
 
 
+@pytest.mark.parametrize("T,E,k", [
+    (3000, 8, 1), (700, 8, 4), (2000, 16, 3), (5000, 4, 4), (600, 8, 3),
+])
+def test_dispatch_bit_exact_general_k(T, E, k):
+    """k distinct experts per token, drawn at random; T * k spans both sides
+    of the 2048-pair switch to the one-workgroup-per-256-pairs kernel."""
+    say(f"dispatch T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 7 + E * 3 + k)
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    off_ref, st_ref, inv_ref = oracle.dispatch_ref(idx, E)
+    off, st, inv = moe.moe_dispatch(to_dev(idx), E)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(off), off_ref)
+    assert np.array_equal(to_host(st), st_ref)
+    assert np.array_equal(to_host(inv), inv_ref)
+
+
 # ---------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------
