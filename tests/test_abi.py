@@ -3,6 +3,8 @@ validates arguments before launching anything (no GPU needed)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -193,3 +195,23 @@ def test_attention_workspace_size(lib):
     ws = lib.moe_attention_workspace_size(ctypes.byref(attn_shape(T=T, d=d, H=H, G=G, d_h=dh)))
     need = T * d * 2 + T * (H + 2 * G) * dh * 4 + T * H * dh * 2 * 2 + T * G * dh * 2 * 2 + T * d * 4
     assert need + GEMM_PARTIALS <= ws < need + GEMM_PARTIALS + (1 << 20)
+
+
+def test_c99_client_compiles_links_and_runs(tmp_path):
+    """The header is plain C: a C99 client builds with -pedantic -Werror,
+    links against libmoe.so and gets the host-side answers and errors."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmoe.so not built")
+    exe = str(tmp_path / "abi_client")
+    src = os.path.join(ROOT, "tests", "c_client", "abi_client.c")
+    build = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I",
+                            os.path.join(ROOT, "include"), src, "-L", lib_dir, "-lmoe",
+                            f"-Wl,-rpath,{lib_dir}", "-o", exe], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert "k = 9 rejected" in run.stdout
