@@ -242,9 +242,10 @@ hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, cons
                                  const uint16_t* b3, uint16_t* h, int64_t T, int d, int d_ff, int E,
                                  hipStream_t stream) {
   const Proj p{w1, w3, b1, b3, h};
-  // Few tokens touch few experts: narrower work items (16 columns) keep every
-  // workgroup busy; the K split doubles when it divides evenly.
-  if (T <= 4 && d % 1024 == 0)
+  // Few tokens touch few experts (up to about 7 at T = 8): narrower work
+  // items (16 columns) keep every workgroup busy; the K split doubles when it
+  // divides evenly.
+  if (T <= 8 && d % 1024 == 0)
     return launch_mb<1, 8, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
   return launch_mb<2, 4, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
 }
@@ -253,9 +254,10 @@ hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, co
                                    const uint16_t* b2, float* y_sorted, int64_t T, int d, int d_ff, int E,
                                    hipStream_t stream) {
   const Proj p{w2, nullptr, b2, nullptr, y_sorted};
-  // With 1-4 tokens only 2-5 experts are touched: an 8-way K split keeps
-  // enough loads in flight when it divides evenly.
-  if (T <= 4 && d_ff % 1024 == 0)
+  // With 1-8 tokens only 2-7 experts are touched: an 8-way K split keeps
+  // enough loads in flight when it divides evenly (at T = 8 it takes the
+  // layer from 399 to 386 us).
+  if (T <= 8 && d_ff % 1024 == 0)
     return launch_mb<1, 8, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
   if (T <= 4) return launch_mb<1, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
   return launch_mb<2, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);

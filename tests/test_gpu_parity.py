@@ -186,6 +186,8 @@ def test_combine_residual_may_alias_output():
     (1000, 256, 384, "bf16", "gemm"),
     (5, 512, 1024, "bf16", "stream"),
     (3, 1024, 1024, "bf16", "stream"),
+    (8, 1024, 2048, "bf16", "stream"),    # 16-column items, 8-way K split, up and down
+    (6, 2048, 1024, "bf16", "stream"),
     (2, 512, 1024, "bf16", "stream"),
     (16, 512, 1536, "bf16", "stream"),
     (30, 1024, 512, "bf16", "stream"),
