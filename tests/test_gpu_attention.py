@@ -80,9 +80,9 @@ def test_gqa_attention_is_deterministic_and_causal():
     assert torch.equal(a[:300], c[:300]) and not torch.equal(a[300:], c[300:])
 
 
-def _sublayer_case(T, d, H, G, pos0, theta, gamma):
+def _sublayer_case(T, d, H, G, pos0, theta, gamma, cfg_id=None):
     say(f"attention sublayer T={T} d={d} H={H} G={G} pos0={pos0} theta={theta} gamma={gamma}")
-    inp = attention_inputs(T, d, H, G, 128, cfg_id=50 + T % 7, gamma=gamma)
+    inp = attention_inputs(T, d, H, G, 128, cfg_id=50 + T % 7 if cfg_id is None else cfg_id, gamma=gamma)
     h = to_dev(inp["h"])
     moe.moe_attention_block_forward(h, to_dev(inp["gamma"]), 1e-5, to_dev(inp["wqkv"]), to_dev(inp["wo"]), H, G,
                                     rope_theta=theta, pos0=pos0)
@@ -113,3 +113,11 @@ def test_attention_sublayer_mixtral_width():
     """Mixtral 8x7B widths (d = 4096, 32 query heads, 8 K/V groups, d_h = 128),
     1024 tokens: every output element against the oracle."""
     _sublayer_case(1024, 4096, 32, 8, 0, 1e6, "ones")
+
+
+def test_attention_sublayer_mixtral_t4096():
+    """The benchmarked sublayer: T = 4096 at Mixtral 8x7B widths (d = 4096,
+    32 query heads, 8 K/V groups, theta = 1e6) on the inputs bench.py times
+    (attention_inputs with its default seed): every output element against
+    the oracle."""
+    _sublayer_case(4096, 4096, 32, 8, 0, 1e6, "ones", cfg_id=40)
