@@ -379,6 +379,15 @@ def test_mixtral_decode_t16_full():
     _mixtral_case("mixtral_decode_t16", lambda cfg, c, i, cl: np.nonzero(cl)[0])
 
 
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_mixtral_decode_small_t_full(T):
+    """The small-T decode layers of the latency sweep (Mixtral decode weights,
+    T = 1 .. 8 tokens, the 16-column / 8-way-K-split streaming shapes): every
+    token against the oracle."""
+    cfg = CONFIGS["mixtral_decode_t16"].with_(name=f"mixtral_decode_t{T}", T=T)
+    _mixtral_case(cfg, lambda cfg, c, i, cl: np.nonzero(cl)[0])
+
+
 def test_mixtral_prefill_t4096_sampled():
     _mixtral_case("mixtral_prefill_t4096", _sample_tokens)
 
