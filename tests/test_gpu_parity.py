@@ -388,6 +388,29 @@ def test_mixtral_decode_small_t_full(T):
     _mixtral_case(cfg, lambda cfg, c, i, cl: np.nonzero(cl)[0])
 
 
+def test_ep_rank_share_sampled():
+    """One expert-parallel rank's share as bench.py times it: 1024 rows through
+    one local expert at full width (d = 4096, d_ff = 14336; a second, empty
+    expert in the layout), on the grouped GEMM.  Sampled rows against the
+    oracle, which computes just those rows."""
+    rows = 1024
+    cfg = CONFIGS["mixtral_prefill_t4096"].with_(name="ep_rank_t4096", T=rows, E=2, k=1)
+    say("ep rank share: generating")
+    dv = generate_torch(cfg, torch.device("cuda:0"))
+    dev = dv["x"].device
+    off = torch.tensor([0, rows, rows], dtype=torch.int32, device=dev)
+    st = torch.arange(rows, dtype=torch.int32, device=dev)
+    ys = moe.moe_expert_ffn(dv["x"], off, st, dv["w1"], dv["w3"], dv["w2"], k=1)
+    torch.cuda.synchronize()
+    picks = np.array(sorted({0, 1, 255, 256, 511, 767, 1023, *np.random.default_rng(3).integers(0, rows, 9).tolist()}),
+                     dtype=np.int32)
+    say(f"ep rank share: oracle on {len(picks)} rows")
+    off_s = np.array([0, len(picks), len(picks)], dtype=np.int32)
+    ref = oracle.expert_rows_ref(to_host(dv["x"]), picks, off_s, to_host(dv["w1"]), to_host(dv["w3"]),
+                                 to_host(dv["w2"]))
+    assert max_rel_err(to_host(ys)[picks], ref) <= BF16_TOL
+
+
 def test_mixtral_prefill_t4096_sampled():
     _mixtral_case("mixtral_prefill_t4096", _sample_tokens)
 
