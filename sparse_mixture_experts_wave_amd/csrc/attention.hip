@@ -7,7 +7,9 @@
 // Kernels here: a row RMSNorm, the RoPE rotation that also splits the fused
 // Q|K|V projection into bf16 head-major tensors, the causal GQA flash
 // attention, and the residual add after W_O.  The two projections run on the
-// grouped MFMA GEMM of the experts (one "expert", no gather).
+// grouped MFMA GEMM of the experts (one "expert", no gather); on that path the
+// GEMM's epilogue does the residual add itself, and the kernel here serves the
+// streaming projection of a few tokens.
 //
 // RoPE reading: the page defers the rotation to another chapter; its
 // HuggingFace loader permutes the rows of q_proj / k_proj per head, which

@@ -342,12 +342,15 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int cus, int KT, bool
 // fp32 (down).  32x32 accumulator layout: lane holds column lane%32 and rows
 // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Gated: the W1 and W3
 // bias of the lane's one column.
-// Only the 32-row blocks mi in [mlo, mhi) of each wave are stored.
+// Only the 32-row blocks mi in [mlo, mhi) of each wave are stored.  With
+// resid set (not gated) the fp32 result is not stored: it is added to the bf16
+// matrix resid in place with one rounding, resid = bf16(resid + (acc + bias)),
+// the residual connection after an output projection.
 template <bool GATED>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4][2],
                                            const uint16_t* __restrict__ bias0,
-                                           const uint16_t* __restrict__ bias1, void* __restrict__ out, int N,
-                                           int mlo = 0, int mhi = 4) {
+                                           const uint16_t* __restrict__ bias1, void* __restrict__ out,
+                                           uint16_t* __restrict__ resid, int N, int mlo = 0, int mhi = 4) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2;
@@ -358,6 +361,38 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
     const int n = GATED ? t.n0 + wn * 32 + (lane & 31) : t.n0 + wn * 64 + nb * 32 + (lane & 31);
     const uint16_t* bsrc = (GATED && nb == 1) ? bias1 : bias0;
     bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
+  }
+  if constexpr (!GATED) {
+    if (resid) {
+      // Per 32-row block: every residual load is issued before the first
+      // store, so their latencies overlap.  The loads are unconditional (rows
+      // and columns past the tile's edge are clamped to its last valid one)
+      // so that no branch forces a wait between them.
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        if (mi < mlo || mi >= mhi) continue;
+        uint16_t hv[16][2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int r = min(wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), t.rows - 1);
+            const int n = min(t.n0 + wn * 64 + nb * 32 + (lane & 31), N - 1);
+            hv[v][nb] = resid[static_cast<int64_t>(t.m0 + r) * N + n];
+          }
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
+            if (r < t.rows && n < N)
+              resid[static_cast<int64_t>(t.m0 + r) * N + n] =
+                  f32_to_bf16(bf16_to_f32(hv[v][nb]) + (acc[mi][nb][v] + bb[nb]));
+          }
+      }
+      return;
+    }
   }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -400,8 +435,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
-    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int NT,
-    float4* __restrict__ part, int cus) {
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, uint16_t* __restrict__ resid, int N, int K,
+    int NT, float4* __restrict__ part, int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;  // output columns per tile
   // Work unit -> tile (and K piece).  Units past the last one exit.
   const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, part != nullptr);
@@ -481,7 +516,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
   if (piece >= 0)
     store_partial(part + static_cast<int64_t>(piece) * ACC_CHUNKS * NTHR, acc);
   else
-    store_tile<GATED>(t, acc, bias0, bias1, out, N);
+    store_tile<GATED>(t, acc, bias0, bias1, out, resid, N);
 }
 
 // Fix-up of the split tiles: workgroup 4 b + mi sums, for 32-row block mi of
@@ -492,8 +527,9 @@ template <bool GATED>
 __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restrict__ offsets, int E,
                                                           const uint16_t* __restrict__ bias0,
                                                           const uint16_t* __restrict__ bias1,
-                                                          void* __restrict__ out, int N, int K, int NT,
-                                                          const float4* __restrict__ part, int cus) {
+                                                          void* __restrict__ out, uint16_t* __restrict__ resid,
+                                                          int N, int K, int NT, const float4* __restrict__ part,
+                                                          int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, true);
   const int b = blockIdx.x >> 2, mb = blockIdx.x & 3;
@@ -525,7 +561,7 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
         }
     }
   }
-  store_tile<GATED>(t, acc, bias0, bias1, out, N, mb, mb + 1);
+  store_tile<GATED>(t, acc, bias0, bias1, out, resid, N, mb, mb + 1);
 }
 
 // Workgroups that run at once: one per CU (the LDS ring takes a CU's LDS),
@@ -540,8 +576,8 @@ int concurrent_tiles() {
 
 template <bool GATED>
 hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const uint16_t* B0,
-                  const uint16_t* B1, const uint16_t* bias0, const uint16_t* bias1, void* out, int64_t rows,
-                  int N, int K, int E, float* part, hipStream_t s) {
+                  const uint16_t* B1, const uint16_t* bias0, const uint16_t* bias1, void* out, uint16_t* resid,
+                  int64_t rows, int N, int K, int E, float* part, hipStream_t s) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const int NT = (N + COLS - 1) / COLS;
   const int cus = concurrent_tiles();
@@ -557,12 +593,12 @@ hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offse
   const int64_t units = part ? tiles + cus : tiles;
   float4* p4 = reinterpret_cast<float4*>(part);
   gemm_bf16_kernel<GATED><<<static_cast<unsigned>(units), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0,
-                                                                         bias1, out, N, K, NT, p4, cus);
+                                                                         bias1, out, resid, N, K, NT, p4, cus);
   const hipError_t err = hipGetLastError();
   if (part == nullptr || err != hipSuccess) return err;
   // The split tiles number at most cus / 2 (S >= 2), four workgroups each.
-  gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2 * 4), NTHR, 0, s>>>(offsets, E, bias0, bias1, out, N, K,
-                                                                               NT, p4, cus);
+  gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2 * 4), NTHR, 0, s>>>(offsets, E, bias0, bias1, out,
+                                                                               resid, N, K, NT, p4, cus);
   return hipGetLastError();
 }
 
@@ -572,13 +608,20 @@ hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const 
                                const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
                                const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
                                float* part, hipStream_t stream) {
-  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, T * k, d_ff, d, E, part, stream);
+  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, nullptr, T * k, d_ff, d, E, part, stream);
 }
 
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
                                  int E, float* part, hipStream_t stream) {
-  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, T * k, d, d_ff, E, part, stream);
+  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, nullptr, T * k, d, d_ff, E, part,
+                       stream);
+}
+
+hipError_t launch_gemm_down_residual_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
+                                          const uint16_t* b, uint16_t* resid, int64_t rows, int N, int K, int E,
+                                          float* part, hipStream_t stream) {
+  return launch<false>(a, nullptr, offsets, w, nullptr, b, nullptr, nullptr, resid, rows, N, K, E, part, stream);
 }
 
 }  // namespace moe

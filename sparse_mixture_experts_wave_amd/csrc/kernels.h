@@ -68,6 +68,11 @@ hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const 
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
                                  int E, float* part, hipStream_t stream);
+// The down form with the residual connection fused into the epilogue: no fp32
+// output; resid[rows][N] (bf16, row-contiguous) += a . w^T (+ b), one rounding.
+hipError_t launch_gemm_down_residual_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
+                                          const uint16_t* b, uint16_t* resid, int64_t rows, int N, int K, int E,
+                                          float* part, hipStream_t stream);
 
 // Router load-balancing loss over [layers][T][E] logits (aux_loss.hip).
 int aux_loss_max_k();

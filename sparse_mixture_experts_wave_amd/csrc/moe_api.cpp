@@ -468,6 +468,12 @@ moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inou
   MOE_TRY(hip_status(moe::launch_rope_pack(qkv, q, k, v, T, H, G, dh, static_cast<double>(rope_theta), pos0, st),
                      "rope launch"));
   MOE_TRY(hip_status(moe::launch_flash_attn(q, k, v, o, T, H, G, dh, st), "attention launch"));
+  // On the GEMM path the residual add runs in the projection's epilogue; the
+  // streaming path (a few tokens) writes fp32 and adds it after.
+  if (!moe::stream_supported(T, d, nq))
+    return hip_status(moe::launch_gemm_down_residual_bf16(o, off, static_cast<const uint16_t*>(wo), nullptr, h, T, d,
+                                                          nq, 1, part, st),
+                      "output projection launch");
   MOE_TRY(hip_status(moe::launch_expert_down_bf16(o, off, static_cast<const uint16_t*>(wo), nullptr, oproj, T, 1, d,
                                                   nq, 1, part, st),
                      "output projection launch"));
