@@ -200,8 +200,9 @@ typedef struct {
 
 /* Bytes of workspace moe_attention_block_forward needs (normalised input,
  * projections, rotated heads, attention output and, for T > 64, the GEMM
- * partial sums as for moe_workspace_size).  0 for an invalid or unsupported
- * shape.  Host only. */
+ * partial sums as for moe_workspace_size; for T <= 64 an fp32 [T][d] output
+ * projection instead, as above that size the GEMM adds it into h directly).
+ * 0 for an invalid or unsupported shape.  Host only. */
 size_t moe_attention_workspace_size(const moe_attn_shape* shape);
 
 /* Causal GQA attention core on rotated heads:

@@ -8,8 +8,9 @@
 // Q|K|V projection into bf16 head-major tensors, the causal GQA flash
 // attention, and the residual add after W_O.  The two projections run on the
 // grouped MFMA GEMM of the experts (one "expert", no gather); on that path the
-// GEMM's epilogue does the residual add itself, and the kernel here serves the
-// streaming projection of a few tokens.
+// GEMM's epilogues do the RoPE split (from the angle table the RMSNorm kernel
+// writes) and the residual add themselves, and the RoPE and residual kernels
+// here serve the streaming projections of a few tokens.
 //
 // RoPE reading: the page defers the rotation to another chapter; its
 // HuggingFace loader permutes the rows of q_proj / k_proj per head, which
@@ -40,9 +41,26 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int RN_T = 256;
 
+// RoPE angle of pair i of a d_h-wide head at position pos, (cos, sin).  The
+// angle is taken in fp64: positions reach 10^4 .. 10^5 and an fp32 angle would
+// be off by up to ~1e-2 rad there.
+__device__ __forceinline__ float2 rope_angle(int64_t pos, int i, int dh, double theta) {
+  const double ang = static_cast<double>(pos) * pow(theta, -2.0 * i / dh);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  return make_float2(static_cast<float>(cd), static_cast<float>(sd));
+}
+
+// With cs set, workgroup t also writes the angles of position pos0 + t for
+// the 64 pairs of a 128-wide head: cs[t][i], for the projection's epilogue.
 __global__ __launch_bounds__(RN_T) void rmsnorm_rows_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ gamma, float eps,
-                                                            uint16_t* __restrict__ u, int d) {
+                                                            uint16_t* __restrict__ u, int d,
+                                                            float2* __restrict__ cs, double theta, int64_t pos0) {
+  static_assert(RN_T >= 64, "one thread per angle");
+  if (cs && threadIdx.x < 64)
+    cs[static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x] =
+        rope_angle(pos0 + blockIdx.x, static_cast<int>(threadIdx.x), 128, theta);
   __shared__ float part[RN_T / kWave];
   const uint16_t* xr = x + static_cast<int64_t>(blockIdx.x) * d;
   uint16_t* ur = u + static_cast<int64_t>(blockIdx.x) * d;
@@ -85,12 +103,8 @@ __global__ __launch_bounds__(256) void rope_pack_kernel(const float* __restrict_
   if (idx >= T * half) return;
   const int64_t t = idx / half;
   const int i = static_cast<int>(idx - t * half);
-  // The angle in fp64: positions reach 10^4 .. 10^5 and an fp32 angle would be
-  // off by up to ~1e-2 rad there.
-  const double ang = static_cast<double>(pos0 + t) * pow(theta, -2.0 * i / dh);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  const float c = static_cast<float>(cd), s = static_cast<float>(sd);
+  const float2 a = rope_angle(pos0 + t, i, dh, theta);
+  const float c = a.x, s = a.y;
   const float* row = qkv + t * static_cast<int64_t>(H + 2 * G) * dh + 2 * i;
   // Unrolled so that several heads' loads are in flight at once.
 #pragma unroll 8
@@ -410,8 +424,9 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 }  // namespace
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
-                               hipStream_t stream) {
-  rmsnorm_rows_kernel<<<static_cast<unsigned>(T), RN_T, 0, stream>>>(x, gamma, eps, u, d);
+                               hipStream_t stream, float* cs, double theta, int64_t pos0) {
+  rmsnorm_rows_kernel<<<static_cast<unsigned>(T), RN_T, 0, stream>>>(x, gamma, eps, u, d,
+                                                                     reinterpret_cast<float2*>(cs), theta, pos0);
   return hipGetLastError();
 }
 

@@ -338,6 +338,26 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int cus, int KT, bool
   return p;
 }
 
+// Destination of the fused Q|K|V projection of attention, with RoPE: of the N
+// output columns, [0, nq) go to q, [nq, nq + nkv) to k, the rest to v, each a
+// bf16 row-major [rows][width] matrix.  In q and k the pair of columns
+// (2i, 2i+1) of each 128-wide head is turned by the angle whose cosine and
+// sine are cs[row][i] (x0, x1 -> x0 c - x1 s, x0 s + x1 c).  q == nullptr:
+// not this epilogue.
+struct RopeOut {
+  uint16_t* q;
+  uint16_t* k;
+  uint16_t* v;
+  const float2* cs;  // [rows][64]
+  int nq, nkv;
+};
+
+// The value of the neighbouring lane of the pair (lane ^ 1): columns 2i and
+// 2i+1 of one row sit in adjacent lanes of the accumulator layout.
+__device__ __forceinline__ float swap_pair(float y) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, y), 0xB1, 0xF, 0xF, false));
+}
+
 // Epilogue of one tile: biases, then SiLU(gate) * up rounded to bf16 (up) or
 // fp32 (down).  32x32 accumulator layout: lane holds column lane%32 and rows
 // 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Gated: the W1 and W3
@@ -345,12 +365,14 @@ __device__ __forceinline__ SplitPlan split_plan(int total, int cus, int KT, bool
 // Only the 32-row blocks mi in [mlo, mhi) of each wave are stored.  With
 // resid set (not gated) the fp32 result is not stored: it is added to the bf16
 // matrix resid in place with one rounding, resid = bf16(resid + (acc + bias)),
-// the residual connection after an output projection.
+// the residual connection after an output projection.  With ro.q set (not
+// gated) the result goes to q, k, v as RopeOut describes.
 template <bool GATED>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4][2],
                                            const uint16_t* __restrict__ bias0,
                                            const uint16_t* __restrict__ bias1, void* __restrict__ out,
-                                           uint16_t* __restrict__ resid, int N, int mlo = 0, int mhi = 4) {
+                                           uint16_t* __restrict__ resid, const RopeOut& ro, int N,
+                                           int mlo = 0, int mhi = 4) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2;
@@ -363,6 +385,55 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
     bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
   }
   if constexpr (!GATED) {
+    if (ro.q) {
+      // The wave's 64 columns lie in one 128-wide head (N, nq and nkv are
+      // multiples of 128), so the destination is wave-uniform.
+      const int nw = t.n0 + wn * 64;
+      if (nw >= N) return;
+      uint16_t* dst = ro.v;
+      int ld = ro.nkv, c0 = nw - ro.nq - ro.nkv;
+      bool rot = false;
+      if (nw < ro.nq) {
+        dst = ro.q, ld = ro.nq, c0 = nw, rot = true;
+      } else if (nw < ro.nq + ro.nkv) {
+        dst = ro.k, ld = ro.nkv, c0 = nw - ro.nq, rot = true;
+      }
+      const bool odd = lane & 1;
+      const int i0 = ((c0 & 127) + (lane & 31)) >> 1;  // pair index of column nb = 0; nb = 1 adds 16
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        if (mi < mlo || mi >= mhi) continue;
+        // The block's angles first (rows clamped into the tile, as for the
+        // residual loads), so that their loads overlap.
+        float2 cs[16][2];
+        if (rot) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              const int r = min(wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), t.rows - 1);
+              cs[v][nb] = ro.cs[static_cast<int64_t>(t.m0 + r) * 64 + i0 + 16 * nb];
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            float y = acc[mi][nb][v] + bb[nb];
+            if (rot) {
+              // Both lanes of a pair hold the same row, so they take this
+              // branch and the swap together.
+              const float p = swap_pair(y);
+              const float x0 = odd ? p : y, x1 = odd ? y : p;
+              const float c = cs[v][nb].x, sn = cs[v][nb].y;
+              y = odd ? x0 * sn + x1 * c : x0 * c - x1 * sn;
+            }
+            if (r < t.rows) dst[static_cast<int64_t>(t.m0 + r) * ld + c0 + nb * 32 + (lane & 31)] = f32_to_bf16(y);
+          }
+      }
+      return;
+    }
     if (resid) {
       // Per 32-row block: every residual load is issued before the first
       // store, so their latencies overlap.  The loads are unconditional (rows
@@ -435,8 +506,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
     const int32_t* __restrict__ offsets, int E, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
-    const uint16_t* __restrict__ bias1, void* __restrict__ out, uint16_t* __restrict__ resid, int N, int K,
-    int NT, float4* __restrict__ part, int cus) {
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, uint16_t* __restrict__ resid, RopeOut ro, int N,
+    int K, int NT, float4* __restrict__ part, int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;  // output columns per tile
   // Work unit -> tile (and K piece).  Units past the last one exit.
   const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, part != nullptr);
@@ -516,7 +587,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
   if (piece >= 0)
     store_partial(part + static_cast<int64_t>(piece) * ACC_CHUNKS * NTHR, acc);
   else
-    store_tile<GATED>(t, acc, bias0, bias1, out, resid, N);
+    store_tile<GATED>(t, acc, bias0, bias1, out, resid, ro, N);
 }
 
 // Fix-up of the split tiles: workgroup 4 b + mi sums, for 32-row block mi of
@@ -528,8 +599,8 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
                                                           const uint16_t* __restrict__ bias0,
                                                           const uint16_t* __restrict__ bias1,
                                                           void* __restrict__ out, uint16_t* __restrict__ resid,
-                                                          int N, int K, int NT, const float4* __restrict__ part,
-                                                          int cus) {
+                                                          RopeOut ro, int N, int K, int NT,
+                                                          const float4* __restrict__ part, int cus) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const SplitPlan plan = split_plan(count_tiles(offsets, E, NT), cus, K / BK, true);
   const int b = blockIdx.x >> 2, mb = blockIdx.x & 3;
@@ -561,7 +632,7 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
         }
     }
   }
-  store_tile<GATED>(t, acc, bias0, bias1, out, resid, N, mb, mb + 1);
+  store_tile<GATED>(t, acc, bias0, bias1, out, resid, ro, N, mb, mb + 1);
 }
 
 // Workgroups that run at once: one per CU (the LDS ring takes a CU's LDS),
@@ -577,7 +648,7 @@ int concurrent_tiles() {
 template <bool GATED>
 hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const uint16_t* B0,
                   const uint16_t* B1, const uint16_t* bias0, const uint16_t* bias1, void* out, uint16_t* resid,
-                  int64_t rows, int N, int K, int E, float* part, hipStream_t s) {
+                  const RopeOut& ro, int64_t rows, int N, int K, int E, float* part, hipStream_t s) {
   constexpr int COLS = GATED ? BNR / 2 : BNR;
   const int NT = (N + COLS - 1) / COLS;
   const int cus = concurrent_tiles();
@@ -593,12 +664,12 @@ hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offse
   const int64_t units = part ? tiles + cus : tiles;
   float4* p4 = reinterpret_cast<float4*>(part);
   gemm_bf16_kernel<GATED><<<static_cast<unsigned>(units), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0,
-                                                                         bias1, out, resid, N, K, NT, p4, cus);
+                                                                         bias1, out, resid, ro, N, K, NT, p4, cus);
   const hipError_t err = hipGetLastError();
   if (part == nullptr || err != hipSuccess) return err;
   // The split tiles number at most cus / 2 (S >= 2), four workgroups each.
   gemm_fixup_kernel<GATED><<<static_cast<unsigned>(cus / 2 * 4), NTHR, 0, s>>>(offsets, E, bias0, bias1, out,
-                                                                               resid, N, K, NT, p4, cus);
+                                                                               resid, ro, N, K, NT, p4, cus);
   return hipGetLastError();
 }
 
@@ -608,20 +679,30 @@ hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const 
                                const uint16_t* w1, const uint16_t* w3, const uint16_t* b1,
                                const uint16_t* b3, uint16_t* h, int64_t T, int k, int d, int d_ff, int E,
                                float* part, hipStream_t stream) {
-  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, nullptr, T * k, d_ff, d, E, part, stream);
+  return launch<true>(x, sorted_token, offsets, w1, w3, b1, b3, h, nullptr, RopeOut{}, T * k, d_ff, d, E, part,
+                      stream);
 }
 
 hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                  const uint16_t* b2, float* y_sorted, int64_t T, int k, int d, int d_ff,
                                  int E, float* part, hipStream_t stream) {
-  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, nullptr, T * k, d, d_ff, E, part,
-                       stream);
+  return launch<false>(h, nullptr, offsets, w2, nullptr, b2, nullptr, y_sorted, nullptr, RopeOut{}, T * k, d, d_ff,
+                       E, part, stream);
 }
 
 hipError_t launch_gemm_down_residual_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
                                           const uint16_t* b, uint16_t* resid, int64_t rows, int N, int K, int E,
                                           float* part, hipStream_t stream) {
-  return launch<false>(a, nullptr, offsets, w, nullptr, b, nullptr, nullptr, resid, rows, N, K, E, part, stream);
+  return launch<false>(a, nullptr, offsets, w, nullptr, b, nullptr, nullptr, resid, RopeOut{}, rows, N, K, E, part,
+                       stream);
+}
+
+hipError_t launch_gemm_qkv_rope_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
+                                     const float* cs, uint16_t* q, uint16_t* k, uint16_t* v, int64_t rows, int nq,
+                                     int nkv, int K, float* part, hipStream_t stream) {
+  const RopeOut ro{q, k, v, reinterpret_cast<const float2*>(cs), nq, nkv};
+  return launch<false>(a, nullptr, offsets, w, nullptr, nullptr, nullptr, nullptr, nullptr, ro, rows, nq + 2 * nkv,
+                       K, 1, part, stream);
 }
 
 }  // namespace moe

@@ -73,18 +73,27 @@ hipError_t launch_gemm_down_bf16(const uint16_t* h, const int32_t* offsets, cons
 hipError_t launch_gemm_down_residual_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
                                           const uint16_t* b, uint16_t* resid, int64_t rows, int N, int K, int E,
                                           float* part, hipStream_t stream);
+// The fused Q|K|V projection of attention (one expert owning all rows, no
+// bias) with RoPE in the epilogue: q [rows][nq], k, v [rows][nkv] bf16 get the
+// columns of a . w^T, q and k turned by cs [rows][64] (cos, sin) pairs of
+// 128-wide heads.  nq and nkv are multiples of 128.
+hipError_t launch_gemm_qkv_rope_bf16(const uint16_t* a, const int32_t* offsets, const uint16_t* w,
+                                     const float* cs, uint16_t* q, uint16_t* k, uint16_t* v, int64_t rows, int nq,
+                                     int nkv, int K, float* part, hipStream_t stream);
 
 // Router load-balancing loss over [layers][T][E] logits (aux_loss.hip).
 int aux_loss_max_k();
 hipError_t launch_aux_loss(const float* logits, int64_t layers, int64_t T, int E, int k, const uint8_t* mask,
                            float alpha, float* loss, float* stats, hipStream_t stream);
 
-// Attention sublayer (attention.hip): row RMSNorm (bf16 -> bf16), RoPE +
-// split of the fused Q|K|V projection (fp32 -> bf16 head-major), causal GQA
-// flash attention (bf16, d_h = 128), residual add (h += y, one rounding), and
-// the [0, rows] offsets that let the expert GEMM run one dense projection.
+// Attention sublayer (attention.hip): row RMSNorm (bf16 -> bf16; with cs set
+// it also writes the RoPE table cs [T][64] (cos, sin) of positions pos0 + t
+// for d_h = 128), RoPE + split of the fused Q|K|V projection (fp32 -> bf16
+// head-major), causal GQA flash attention (bf16, d_h = 128), residual add
+// (h += y, one rounding), and the [0, rows] offsets that let the expert GEMM
+// run one dense projection.
 hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
-                               hipStream_t stream);
+                               hipStream_t stream, float* cs = nullptr, double theta = 0.0, int64_t pos0 = 0);
 hipError_t launch_rope_pack(const float* qkv, uint16_t* q, uint16_t* k, uint16_t* v, int64_t T, int H, int G,
                             int dh, double theta, int64_t pos0, hipStream_t stream);
 bool flash_attn_supported(int dh);

@@ -241,7 +241,7 @@ moe_status check_attn_shape(const moe_attn_shape* s) {
 }
 
 struct AttnLayout {
-  size_t offsets, xn, qkv, q, k, v, o, oproj, part, total;
+  size_t offsets, xn, qkv, cs, q, k, v, o, oproj, part, total;
 };
 
 AttnLayout attn_layout(const moe_attn_shape* s) {
@@ -251,12 +251,22 @@ AttnLayout attn_layout(const moe_attn_shape* s) {
   size_t at = 0;
   L.offsets = at; at += up(2 * 4);
   L.xn = at; at += up(T * s->d * 2);
-  L.qkv = at; at += up(T * (nq + 2 * nkv) * 4);
+  // The fp32 Q|K|V projection before RoPE: only the streaming path of a few
+  // tokens writes it.  The GEMM path rotates in its epilogue, reading the
+  // (cos, sin) table [T][64] that the RMSNorm kernel writes.
+  const bool qkv_stream = moe::stream_supported(s->T, static_cast<int>(nq + 2 * nkv), s->d);
+  L.qkv = at;
+  if (qkv_stream) at += up(T * (nq + 2 * nkv) * 4);
+  L.cs = at;
+  if (!qkv_stream) at += up(T * 64 * 8);
   L.q = at; at += up(T * nq * 2);
   L.k = at; at += up(T * nkv * 2);
   L.v = at; at += up(T * nkv * 2);
   L.o = at; at += up(T * nq * 2);
-  L.oproj = at; at += up(T * s->d * 4);
+  // The fp32 output projection before the residual add: only the streaming
+  // path of a few tokens writes it (the GEMM adds into h in its epilogue).
+  L.oproj = at;
+  if (moe::stream_supported(s->T, s->d, static_cast<int>(nq))) at += up(T * s->d * 4);
   // The projections' GEMM partial sums (one buffer, used by one projection at a time).
   const size_t pb = std::max(moe::gemm_partial_bytes(s->T, static_cast<int>(nq + 2 * nkv), s->d),
                              moe::gemm_partial_bytes(s->T, s->d, static_cast<int>(nq)));
@@ -460,13 +470,24 @@ moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inou
   const hipStream_t st = hs(stream);
   // The projections run on the experts' GEMM as a single expert owning all T rows.
   MOE_TRY(hip_status(moe::launch_row_range(off, T, st), "row range launch"));
-  MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st), "rmsnorm launch"));
   float* part = L.part < L.total ? at<float>(ws, L.part) : nullptr;
-  MOE_TRY(hip_status(moe::launch_expert_down_bf16(xn, off, static_cast<const uint16_t*>(wqkv), nullptr, qkv, T, 1,
-                                                  nqkv, d, 1, part, st),
-                     "qkv projection launch"));
-  MOE_TRY(hip_status(moe::launch_rope_pack(qkv, q, k, v, T, H, G, dh, static_cast<double>(rope_theta), pos0, st),
-                     "rope launch"));
+  if (!moe::stream_supported(T, nqkv, d)) {
+    // GEMM path: RoPE and the split into q, k, v run in the projection's epilogue.
+    float* cs = at<float>(ws, L.cs);
+    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st, cs, static_cast<double>(rope_theta),
+                                                pos0),
+                       "rmsnorm launch"));
+    MOE_TRY(hip_status(moe::launch_gemm_qkv_rope_bf16(xn, off, static_cast<const uint16_t*>(wqkv), cs, q, k, v, T,
+                                                      nq, G * dh, d, part, st),
+                       "qkv projection launch"));
+  } else {
+    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st), "rmsnorm launch"));
+    MOE_TRY(hip_status(moe::launch_expert_down_bf16(xn, off, static_cast<const uint16_t*>(wqkv), nullptr, qkv, T, 1,
+                                                    nqkv, d, 1, part, st),
+                       "qkv projection launch"));
+    MOE_TRY(hip_status(moe::launch_rope_pack(qkv, q, k, v, T, H, G, dh, static_cast<double>(rope_theta), pos0, st),
+                       "rope launch"));
+  }
   MOE_TRY(hip_status(moe::launch_flash_attn(q, k, v, o, T, H, G, dh, st), "attention launch"));
   // On the GEMM path the residual add runs in the projection's epilogue; the
   // streaming path (a few tokens) writes fp32 and adds it after.

@@ -191,10 +191,21 @@ def test_attention_block_validation(lib):
 
 
 def test_attention_workspace_size(lib):
-    T, d, H, G, dh = 4096, 4096, 32, 8, 128
-    ws = lib.moe_attention_workspace_size(ctypes.byref(attn_shape(T=T, d=d, H=H, G=G, d_h=dh)))
-    need = T * d * 2 + T * (H + 2 * G) * dh * 4 + T * H * dh * 2 * 2 + T * G * dh * 2 * 2 + T * d * 4
-    assert need + GEMM_PARTIALS <= ws < need + GEMM_PARTIALS + (1 << 20)
+    d, H, G, dh = 4096, 32, 8, 128
+
+    def need(T):  # normalised input, q, k, v, o (bf16)
+        return T * d * 2 + T * H * dh * 2 * 2 + T * G * dh * 2 * 2
+
+    # GEMM path: partial sums and the RoPE (cos, sin) table [T][64]; neither
+    # fp32 projection (RoPE and the residual add run in the GEMM epilogues).
+    ws = lib.moe_attention_workspace_size(ctypes.byref(attn_shape(T=4096, d=d, H=H, G=G, d_h=dh)))
+    gemm = need(4096) + 4096 * 64 * 8 + GEMM_PARTIALS
+    assert gemm <= ws < gemm + (1 << 20)
+    # Streaming path (T <= 64): the fp32 Q|K|V and output projections, no
+    # partials, no table.
+    ws = lib.moe_attention_workspace_size(ctypes.byref(attn_shape(T=16, d=d, H=H, G=G, d_h=dh)))
+    stream = need(16) + 16 * (H + 2 * G) * dh * 4 + 16 * d * 4
+    assert stream <= ws < stream + 4096
 
 
 def test_c99_client_compiles_links_and_runs(tmp_path):
