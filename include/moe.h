@@ -198,10 +198,11 @@ typedef struct {
   int32_t act;  /* moe_dtype of activations and weights: BF16 is implemented */
 } moe_attn_shape;
 
-/* Bytes of workspace moe_attention_block_forward needs (normalised input,
- * projections, rotated heads, attention output and, for T > 64, the GEMM
- * partial sums as for moe_workspace_size; for T <= 64 an fp32 [T][d] output
- * projection instead, as above that size the GEMM adds it into h directly).
+/* Bytes of workspace moe_attention_block_forward needs: the normalised
+ * input, the rotated heads and the attention output; for T > 64 the GEMM
+ * partial sums as for moe_workspace_size and a [T][64] table of RoPE
+ * (cos, sin) pairs (the projections' epilogues rotate and add into h
+ * directly); for T <= 64 the fp32 Q|K|V and output projections instead.
  * 0 for an invalid or unsupported shape.  Host only. */
 size_t moe_attention_workspace_size(const moe_attn_shape* shape);
 

@@ -105,6 +105,7 @@ def _sublayer_case(T, d, H, G, pos0, theta, gamma, cfg_id=None):
     (300, 1024, 8, 2, 1000, 1e6, "ones"),
     (64, 512, 4, 4, 30000, 1e6, "random"),
     (150, 256, 3, 1, 7, 1e4, "random"),  # Q|K|V width 640: a half-used last column tile
+    (130, 512, 4, 2, 100000, 1e6, "random"),  # far positions through the GEMM epilogue's angle table
 ])
 def test_attention_sublayer(T, d, H, G, pos0, theta, gamma):
     _sublayer_case(T, d, H, G, pos0, theta, gamma)
