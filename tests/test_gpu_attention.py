@@ -104,6 +104,7 @@ def _sublayer_case(T, d, H, G, pos0, theta, gamma, cfg_id=None):
     (200, 512, 4, 2, 0, 1e6, "random"),
     (300, 1024, 8, 2, 1000, 1e6, "ones"),
     (64, 512, 4, 4, 30000, 1e6, "random"),
+    (65, 512, 4, 4, 30000, 1e6, "random"),  # the same one token past the streaming limit: fused epilogues
     (150, 256, 3, 1, 7, 1e4, "random"),  # Q|K|V width 640: a half-used last column tile
     (130, 512, 4, 2, 100000, 1e6, "random"),  # far positions through the GEMM epilogue's angle table
 ])

@@ -192,6 +192,7 @@ def test_combine_residual_may_alias_output():
     (16, 512, 1536, "bf16", "stream"),
     (30, 1024, 512, "bf16", "stream"),
     (64, 512, 1024, "bf16", "stream"),
+    (65, 512, 1024, "bf16", "gemm"),  # one token past the streaming limit, same widths
     (16, 192, 256, "bf16", "gemm"),   # d not a multiple of 512: small T on the GEMM path
 ])
 def test_expert_ffn(T, d, d_ff, dtype, path):
