@@ -18,13 +18,20 @@
 //
 // Precision: every product x_j * W[e][j] (bf16 or fp32 times fp32) is exact
 // in fp64, and the sums are kept in fp64 until the logit is rounded once to
-// fp32, so the logit is the fp32 value of the exact dot product whatever the
-// summation order (the pages fix the router's precision, fp32, not an order).
+// fp32 (the pages fix the router's precision, fp32, not an order).  The fp64
+// sum of d products is not exact itself: its relative error is at most about
+// d * 2^-53, far below fp32's 2^-24, so the logit is the correctly rounded
+// fp32 value of the exact dot product except when that value lies within
+// the fp64 error of a rounding boundary between two fp32 numbers; then the
+// summation order can move it by one fp32 ulp.  Such a 1-ulp difference can
+// only change the top-k choice of a token whose logits are that close.
 //
 // With gamma != nullptr the kernel also applies RMSNorm: it accumulates
 // sum(x^2) next to the dot products, and since u = x * rinv * gamma the
-// logits are rinv * sum_j (x_j gamma_j) W[e][j]; the normalised rows u are
-// then written (rounded to the activation dtype) for the experts.
+// logits are rinv * sum_j (x_j gamma_j) W[e][j], with rinv the fp32 inverse
+// root of the fp32-rounded mean square: the product with rinv is formed in
+// fp64 and rounded once.  The normalised rows u are then written (rounded to
+// the activation dtype) for the experts.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -131,10 +138,12 @@ __global__ __launch_bounds__(64 * NW) void router_top2_kernel(
     if constexpr (NORM) r[lane * LD + P + t] = ss[t];
   }
   __syncthreads();
-  if (lane < COLS) {
+  // COLS can exceed the 64 lanes (E = 64 with the norm: 64 logits + the sum
+  // of squares), so each lane reduces every 64th column.
+  for (int c = lane; c < COLS; c += 64) {
     double s = 0.0;
-    for (int l = 0; l < 64; ++l) s += r[l * LD + lane];
-    part[wave][lane] = s;
+    for (int l = 0; l < 64; ++l) s += r[l * LD + c];
+    part[wave][c] = s;
   }
   __syncthreads();
 
