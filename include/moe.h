@@ -118,7 +118,8 @@ moe_status moe_route(const moe_shape* shape, const void* x, const float* w_gate,
                      float* topk_w, void* stream);
 
 /* Dispatch: stable counting sort of the T*k (token, slot) pairs by expert,
- * the order of the pages' `where(topk_idx == e)` loop ("Алгоритм").
+ * the order in which the pages' expert loop visits them ("Алгоритм"):
+ * expert by expert, each expert's tokens ascending.
  *   topk_idx       [T][k] int32, entries in 0..E-1 (others are skipped and
  *                  get inv_pos -1)
  *   expert_offsets [E+1] int32 output: rows of expert e are

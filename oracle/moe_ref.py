@@ -16,10 +16,11 @@ Sources (all on the pages this project follows):
   [MIX-IN] same page, section "MoE изнутри" (MoE inside): router is a Linear
            layer, top-k then a softmax over the k kept logits in float32, each
            expert sees only its tokens, output is the weighted sum.
-  [MIX-A]  same page, section "Алгоритм" (algorithm): loop over experts,
-           dispatch each expert's tokens in row-major `where` order, skip
-           empty experts, index-add the weighted expert output; every token
-           gets exactly k terms, dropless, checked against a naive token loop.
+  [MIX-A]  same page, section "Алгоритм" (algorithm): an outer loop over
+           experts, each expert applied to the tokens that selected it (in
+           token order), experts without tokens skipped, the weighted outputs
+           accumulated at their tokens; every token gets exactly k terms
+           (dropless), and the result is checked against a token-by-token loop.
   [MIX-LB] same page, section "Load-balancing loss".
   [MIX-HF] same page, section "Загрузка весов HuggingFace": router w1/w3/w2
            map to gate/up/down.
@@ -177,19 +178,26 @@ def moe_forward_token_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.flo
 # O2: the pages' expert-major algorithm  [MIX-A]
 # ----------------------------------------------------------------------------
 def moe_forward_expert_loop(x, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.float32, eb=None):
-    """Loop over experts: gather the expert's tokens (row-major where), skip empty
-    experts, index-add the weighted expert output into Y ([MIX-A])."""
+    """Expert-major form ([MIX-A]): every expert runs once, on the block of
+    tokens that selected it, and its outputs, scaled by the tokens' combine
+    weights, are added into those tokens' rows of a zero output.
+
+    The blocks are the dispatch permutation (dispatch_ref): expert e's block
+    is rows offsets[e] .. offsets[e+1] of sorted_token, its tokens ascending;
+    an empty block is not evaluated.  Row r of a block belongs to token
+    sorted_token[r] and to the slot s with inv_pos[t, s] = r, whose weight
+    scales it."""
     g, idx, w = route_ref(x, w_gate, bias, k, dtype)
     X = widen(x, dtype)
     T, d = X.shape
     E = widen(w_gate, dtype).shape[0]
+    offsets, sorted_token, inv_pos = dispatch_ref(idx, E)
+    rows = expert_rows_ref(X, sorted_token, offsets, w1, w3, w2, dtype, eb)
+    slot_of_row = np.empty(T * k, dtype=np.int64)
+    slot_of_row[inv_pos.reshape(-1)] = np.tile(np.arange(k), T)
+    scale = w[sorted_token, slot_of_row].astype(dtype)
     Y = np.zeros((T, d), dtype=dtype)
-    for e in range(E):
-        tok, slot = np.nonzero(idx == e)
-        if tok.size == 0:
-            continue
-        out = expert_swiglu(X[tok], w1[e], w3[e], w2[e], dtype, *_expert_bias(eb, e))
-        np.add.at(Y, tok, w[tok, slot][:, None] * out)
+    np.add.at(Y, sorted_token, scale[:, None] * rows)
     return Y, (g, idx, w)
 
 
@@ -207,7 +215,8 @@ def moe_forward_tokens(x_rows, w_gate, bias, w1, w3, w2, k: int = 2, dtype=np.fl
 # dispatch  [MIX-A]
 # ----------------------------------------------------------------------------
 def dispatch_ref(idx: np.ndarray, E: int):
-    """Expert-sorted permutation in the order of the pages' `where(topk_idx == e)`.
+    """Expert-sorted permutation in the order the pages' expert loop visits the
+    (token, slot) pairs ([MIX-A]): expert by expert, each expert's tokens ascending.
 
     Returns (expert_offsets [E+1], sorted_token [T*k], inv_pos [T, k]):
     rows of expert e are sorted_token[offsets[e]:offsets[e+1]], tokens

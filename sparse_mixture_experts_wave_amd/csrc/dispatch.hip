@@ -2,8 +2,7 @@
 //
 // The order is that of the expert-major algorithm on the "Mixtral" textbook
 // page (section "Алгоритм"): for expert e = 0..E-1 the tokens that selected
-// it, ascending (a row-major `where(topk_idx == e)`); empty experts get no
-// rows.  One workgroup does the whole sort with no host round trip:
+// it, in ascending token order; empty experts get no rows.  One workgroup does the whole sort with no host round trip:
 //   1. every thread counts its contiguous run of tokens per expert into its
 //      own LDS column cnt[e][thread];
 //   2. one exclusive scan over cnt in (expert, thread) order gives each

@@ -165,3 +165,118 @@ def test_planted_attention_mistake_is_caught(mutant):
         vv = np.stack([v[:, h % G] for h in range(H)], axis=1)
         got = attn_ref.gqa_attention_ref(q, kk, vv, True, np.float64)
     assert np.max(np.abs(got - _sdpa(q, k, v))) > 1e-2
+
+
+# ---------------------------------------------------------------------------
+# RoPE frequency schedule and pairing against HuggingFace's Mixtral.  The
+# "Mixtral" page ("Загрузка весов HuggingFace") loads HF checkpoints by
+# reordering the rows of q_proj (per query head) and k_proj (per K/V head);
+# with that reordering the library's rotation must reproduce HF's.  HF's
+# rotary module and attention run here offline on a random tiny config.
+# ---------------------------------------------------------------------------
+def _hf_rows_to_interleaved(w, n_heads, dh):
+    """Per head, HF's rotation partners (j, j + dh/2) become rows (2j, 2j + 1)."""
+    w = np.asarray(w)
+    out = np.empty_like(w)
+    for h in range(n_heads):
+        blk = w[h * dh:(h + 1) * dh]
+        dst = out[h * dh:(h + 1) * dh]
+        dst[0::2] = blk[:dh // 2]
+        dst[1::2] = blk[dh // 2:]
+    return out
+
+
+def _hf_mixtral(H, G, dh, d, theta):
+    from transformers import MixtralConfig
+    from transformers.models.mixtral import modeling_mixtral as mm
+
+    cfg = MixtralConfig(hidden_size=d, num_attention_heads=H, num_key_value_heads=G, head_dim=dh, rope_theta=theta,
+                        intermediate_size=32, num_local_experts=4)
+    cfg._attn_implementation = "sdpa"
+    return cfg, mm
+
+
+def _rope_by_hf(x, pos, theta):
+    """x [T, n, dh] rotated by HF's MixtralRotaryEmbedding + apply_rotary_pos_emb (half-split pairs)."""
+    T, n, dh = x.shape
+    cfg, mm = _hf_mixtral(n, n, dh, n * dh, theta)
+    rot = mm.MixtralRotaryEmbedding(cfg)
+    X = torch.from_numpy(np.asarray(x, np.float64)).transpose(0, 1)[None]  # [1, n, T, dh]
+    cos, sin = rot(X, torch.as_tensor(np.asarray(pos))[None])
+    out, _ = mm.apply_rotary_pos_emb(X, X, cos, sin)
+    return out[0].transpose(0, 1).numpy()
+
+
+def _interleave_cols(y):
+    """Columns of a half-split head vector in the interleaved order (j -> 2j, j + dh/2 -> 2j + 1)."""
+    dh = y.shape[-1]
+    out = np.empty_like(y)
+    out[..., 0::2], out[..., 1::2] = y[..., :dh // 2], y[..., dh // 2:]
+    return out
+
+
+@pytest.mark.parametrize("theta,dh", [(1e4, 16), (1e6, 32), (1e6, 128)])
+def test_rope_matches_hf_mixtral_after_row_permutation(theta, dh):
+    """rope_ref of the permuted projection == HF's rotation of the HF projection,
+    column j of HF's head landing on 2j and column j + dh/2 on 2j + 1.  This fixes
+    both the pairing and the schedule theta^(-2i/d_h), including i = 0."""
+    rng = _rng(20 + dh)
+    T, n = 11, 3
+    y_hf = rng.standard_normal((T, n, dh))
+    pos = np.arange(40, 40 + T)
+    want = _interleave_cols(_rope_by_hf(y_hf, pos, theta))
+    got = attn_ref.rope_ref(_interleave_cols(y_hf), pos, theta, np.float64)
+    # HF forms the angles in float32: about p * 2^-24 rad of error per pair
+    assert np.max(np.abs(got - want)) < 1e-4 * np.max(np.abs(want))
+
+
+def test_attention_matches_hf_mixtral_attention():
+    """The oracle's GQA with RoPE and W_O (no norm, no residual) on HF weights whose
+    q_proj / k_proj rows are reordered as the page's loader does == HF's
+    MixtralAttention (sdpa, causal) on the original weights."""
+    rng = _rng(30)
+    T, d, H, G, dh, theta, pos0 = 13, 64, 4, 2, 16, 1e6, 7
+    cfg, mm = _hf_mixtral(H, G, dh, d, theta)
+    att = mm.MixtralAttention(cfg, 0).double()
+    wq = rng.standard_normal((H * dh, d)) / 8
+    wk = rng.standard_normal((G * dh, d)) / 8
+    wv = rng.standard_normal((G * dh, d)) / 8
+    wo = rng.standard_normal((d, H * dh)) / 8
+    with torch.no_grad():
+        for name, w in (("q_proj", wq), ("k_proj", wk), ("v_proj", wv), ("o_proj", wo)):
+            getattr(att, name).weight.copy_(torch.from_numpy(w))
+        x = torch.from_numpy(rng.standard_normal((1, T, d)))
+        cos, sin = mm.MixtralRotaryEmbedding(cfg)(x, torch.arange(pos0, pos0 + T)[None])
+        want, _ = att(x, (cos, sin), None)
+    want = want[0].numpy()
+    X = x[0].numpy()
+    wq_l, wk_l = _hf_rows_to_interleaved(wq, H, dh), _hf_rows_to_interleaved(wk, G, dh)
+    pos = np.arange(pos0, pos0 + T)
+    q = attn_ref.rope_ref((X @ wq_l.T).reshape(T, H, dh), pos, theta, np.float64)
+    k = attn_ref.rope_ref((X @ wk_l.T).reshape(T, G, dh), pos, theta, np.float64)
+    v = (X @ wv.T).reshape(T, G, dh)
+    got = attn_ref.gqa_attention_ref(q, k, v, True, np.float64).reshape(T, H * dh) @ wo.T
+    assert np.max(np.abs(got - want)) < 1e-5 * np.max(np.abs(want))
+
+
+def _rope_wrong_schedule(x, positions, theta, dtype=np.float32):
+    """Planted mistake: theta^(-i/d_h) instead of theta^(-2i/d_h)."""
+    x = np.asarray(x, dtype)
+    dh = x.shape[-1]
+    ang = np.asarray(positions, np.float64)[:, None] * theta ** (-1.0 * np.arange(dh // 2) / dh)
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_rope_wrong_schedule, _rope_half_split])
+def test_planted_rope_mistake_fails_hf_pin(monkeypatch, mutant):
+    monkeypatch.setattr(attn_ref, "rope_ref", mutant)
+    rng = _rng(21)
+    y_hf = rng.standard_normal((11, 3, 32))
+    pos = np.arange(40, 51)
+    want = _interleave_cols(_rope_by_hf(y_hf, pos, 1e6))
+    got = attn_ref.rope_ref(_interleave_cols(y_hf), pos, 1e6, np.float64)
+    assert np.max(np.abs(got - want)) > 1e-2 * np.max(np.abs(want))

@@ -535,3 +535,68 @@ def test_router_stats_are_distributions():
     assert np.all(f[0] + f[1] <= 1.0 + 1e-12)                     # an expert fills at most one slot per token
     f0, P0 = oracle.router_stats_ref(g, 8, 2, np.zeros(50, bool))
     assert not f0.any() and not P0.any()
+
+
+# ---------------------------------------------------------------------------
+# load-balancing loss against HuggingFace's Mixtral ("Load-balancing loss": the
+# page's loss agrees with HF's load_balancing_loss_func up to float; P_i is
+# the mean of the router's softmax over all E experts)
+# ---------------------------------------------------------------------------
+def _hf_lb_loss(logits_per_layer, E, k, mask=None):
+    from transformers.models.mixtral.modeling_mixtral import load_balancing_loss_func
+
+    g = tuple(torch.from_numpy(np.asarray(a, np.float64)) for a in logits_per_layer)
+    m = None if mask is None else torch.from_numpy(np.asarray(mask, np.int64))[None, :]
+    return float(load_balancing_loss_func(g, E, k, m))
+
+
+@pytest.mark.parametrize("E,k,layers,masked", [(8, 2, 1, False), (8, 2, 3, True), (16, 4, 2, False),
+                                                (4, 1, 2, True), (64, 6, 1, True)])
+def test_aux_loss_matches_hf_load_balancing_loss(E, k, layers, masked):
+    rng = np.random.default_rng(E * 10 + k)
+    T = 97
+    # non-uniform logits: a per-expert offset makes P_i differ from the top-k shares
+    g = [rng.standard_normal((T, E)) * 1.5 + np.linspace(-1, 2, E)[None, :] for _ in range(layers)]
+    mask = (rng.uniform(size=T) > 0.25) if masked else None
+    want = _hf_lb_loss(g, E, k, mask)
+    got = oracle.aux_loss_ref(g, E, k, alpha=1.0, token_mask=mask)
+    # HF averages the one-hot top-k mask in float32 (f_{s,i} rounded to fp32)
+    assert abs(got - want) <= 1e-6 * abs(want)
+
+
+def test_router_stats_P_is_mean_full_softmax():
+    rng = np.random.default_rng(3)
+    g = [rng.standard_normal((40, 8)) * 2 for _ in range(2)]
+    mask = rng.uniform(size=40) > 0.3
+    _, P = oracle.router_stats_ref(g, 8, 2, mask)
+    rows = np.concatenate([a[mask] for a in g])
+    np.testing.assert_allclose(P, scipy.special.softmax(rows, axis=1).mean(axis=0), rtol=1e-13)
+
+
+def _mut_stats_topk_P(logits_per_layer, E, k, token_mask=None, dtype=np.float64):
+    """Planted mistake: P_i from the renormalised top-k weights instead of the full softmax."""
+    f, _ = _orig_stats(logits_per_layer, E, k, token_mask, dtype)
+    G = np.concatenate([np.asarray(a, dtype)[np.asarray(token_mask, bool)] if token_mask is not None
+                        else np.asarray(a, dtype) for a in logits_per_layer])
+    idx = moe_ref.top2(G, k)
+    w = moe_ref.topk_softmax(G, idx, dtype)
+    P = np.zeros((G.shape[0], E), dtype)
+    np.put_along_axis(P, idx.astype(np.int64), w, axis=1)
+    return f, P.mean(axis=0)
+
+
+_orig_stats = moe_ref.router_stats_ref
+
+
+def test_planted_topk_P_fails_hf_pin(monkeypatch):
+    monkeypatch.setattr(moe_ref, "router_stats_ref", _mut_stats_topk_P)
+    rng = np.random.default_rng(80)
+    g = [rng.standard_normal((97, 8)) * 1.5 + np.linspace(-1, 2, 8)[None, :]]
+    got = moe_ref.aux_loss_ref(g, 8, 2, alpha=1.0)
+    monkeypatch.undo()
+    want = _hf_lb_loss(g, 8, 2)
+    assert abs(got - want) > 1e-2 * abs(want)
+    # the two closed-form pins cannot tell this mutant apart (both hold for it too)
+    v = np.array([3.0, 2.0, 0.5, 0.1, -0.2, -1.0, -1.5, -2.0])
+    u = np.stack([np.roll(v, s) for s in range(8)])
+    assert abs(_mut_stats_topk_P([u], 8, 2)[1].sum() - 1.0) < 1e-12
