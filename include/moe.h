@@ -166,6 +166,29 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
                        const void* w2, const moe_expert_bias* expert_bias,
                        void* y, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole layer exactly as moe_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument.  The routing,
+ * the permutation, h [T*k][d_ff] and y_sorted [T*k][d] live instead in a
+ * static 64 MiB device buffer inside the library, one per GPU, held until
+ * the process ends.  The call allocates nothing.
+ *   Arguments and errors as moe_forward (y must not alias x).
+ *   Limit: those intermediates must fit 64 MiB.  At Mixtral's shape (d 4096,
+ *   d_ff 14336, bf16, k 2) that is T <= 744 tokens; a larger T returns
+ *   MOE_ERR_UNSUPPORTED and launches nothing.
+ *   Sharing: every call on a GPU uses that GPU's one buffer and leaves its
+ *   contents there; calls that overlap on one GPU (other streams, other
+ *   threads) race and must be serialised by the caller.  Nothing in the
+ *   buffer needs to start zeroed.
+ *   Results: bit-identical to moe_forward on the streaming path (bf16,
+ *   T <= 64) and the fp32 path; on the bf16 GEMM path the last round of GEMM
+ *   tiles is not split along K (moe_forward keeps those partial sums in its
+ *   workspace), so the fp32 sums run in another order.                      */
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_gate,
+                               const float* bias, const void* w1, const void* w3,
+                               const void* w2, const moe_expert_bias* expert_bias,
+                               void* y, void* stream);
+
 /* One pre-norm residual MoE sublayer ("Прямой проход в формулах", block
  * equation H = U + MoE(RMSNorm_2(U)); RMSNorm(z) = z / sqrt(mean z^2 + eps)
  * * gamma), in place on h:

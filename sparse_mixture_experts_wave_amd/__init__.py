@@ -18,6 +18,7 @@ from .moe import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_forward,
+    moe_forward_noalloc,
     moe_route,
     workspace_size,
 )

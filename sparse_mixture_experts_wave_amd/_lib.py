@@ -56,6 +56,7 @@ SIGNATURES = {
     "moe_expert_ffn": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _bp, _vp, _vp, ctypes.c_size_t, _vp]),
     "moe_combine": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_forward": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _bp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "moe_forward_noalloc": (ctypes.c_int, [_sp, _vp, _vp, _vp, _vp, _vp, _vp, _bp, _vp, _vp]),
     "moe_block_forward": (ctypes.c_int, [_sp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _bp, _vp,
                                          ctypes.c_size_t, _vp]),
     "moe_aux_loss": (ctypes.c_int, [_sp, _vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp, _vp]),

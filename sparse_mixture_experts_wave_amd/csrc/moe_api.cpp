@@ -1,14 +1,16 @@
 // C ABI of the MoE layer: argument validation, workspace carving and the
 // launch sequence route -> dispatch -> experts -> combine (and, for the
-// attention sublayer, rmsnorm -> qkv -> rope -> attention -> output -> residual).  Host code only;
+// attention sublayer, rmsnorm -> qkv -> rope -> attention -> output -> residual).  Host code,
+// plus one static device array (the scratch buffer of moe_forward_noalloc);
 // every launch is asynchronous on the caller's stream and nothing here
 // synchronises or reads device memory.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -100,7 +102,7 @@ size_t part_bytes(const moe_shape* s) {
   return s->wt == MOE_BF16 ? moe::gemm_partial_bytes(s->T, s->d, s->d_ff) : 0;
 }
 
-Layout layout(const moe_shape* s, bool block) {
+Layout layout(const moe_shape* s, bool block, bool with_part = true) {
   const size_t rows = static_cast<size_t>(s->T) * s->k;
   Layout L{};
   size_t at = 0;
@@ -112,7 +114,7 @@ Layout layout(const moe_shape* s, bool block) {
   L.h = at; at += up(rows * s->d_ff * esize(s->wt));
   L.y_sorted = at; at += up(rows * s->d * 4);
   L.u = at; if (block) at += up(static_cast<size_t>(s->T) * s->d * esize(s->act));
-  L.part = at; at += up(part_bytes(s));
+  L.part = at; if (with_part) at += up(part_bytes(s));
   L.total = at;
   return L;
 }
@@ -188,9 +190,9 @@ moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const 
 moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, const float* bias,
                         const void* w1, const void* w3, const void* w2, const moe_expert_bias* eb, void* y,
                         const void* residual, const float* gamma, float eps, void* ws, size_t ws_bytes,
-                        void* stream) {
+                        void* stream, bool with_part = true) {
   const bool block = gamma != nullptr;
-  const Layout L = layout(s, block);
+  const Layout L = layout(s, block, with_part);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", ws_bytes, L.total);
   int32_t* idx = at<int32_t>(ws, L.topk_idx);
@@ -211,12 +213,46 @@ moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, 
   MOE_TRY(mark(1, stream));
   MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
   MOE_TRY(mark(2, stream));
-  float* part = part_bytes(s) ? at<float>(ws, L.part) : nullptr;
+  float* part = (with_part && part_bytes(s)) ? at<float>(ws, L.part) : nullptr;
   MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, part, stream, true));
   MOE_TRY(mark(4, stream));
   MOE_TRY(hip_status(moe::launch_combine(ys, inv, w, residual, y, s->act == MOE_BF16, s->T, s->k, s->d, hs(stream)),
                      "combine launch"));
   return mark(5, stream);
+}
+
+// ---------------------------------------------------------------------------
+// the layer without a caller workspace (moe_forward_noalloc)
+// ---------------------------------------------------------------------------
+// The intermediates of one moe_forward_noalloc call (routing, permutation, h,
+// y_sorted; no GEMM partial sums) live in this array.  Every GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// `scratch` is only a host-side stand-in for the symbol: kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(err));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -373,6 +409,32 @@ moe_status moe_forward(const moe_shape* shape, const void* x, const float* w_gat
   MOE_TRY(need(ws, "ws"));
   return forward_impl(shape, x, w_gate, bias, w1, w3, w2, expert_bias, y, nullptr, nullptr, 0.f, ws, ws_bytes,
                       stream);
+}
+
+moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const float* w_gate, const float* bias,
+                               const void* w1, const void* w3, const void* w2, const moe_expert_bias* expert_bias,
+                               void* y, void* stream) {
+  MOE_TRY(check_shape(shape));
+  if (shape->T == 0) return ok();
+  MOE_TRY(need(x, "x"));
+  MOE_TRY(need(w_gate, "w_gate"));
+  MOE_TRY(optional(bias, "bias"));
+  MOE_TRY(need(w1, "w1"));
+  MOE_TRY(need(w3, "w3"));
+  MOE_TRY(need(w2, "w2"));
+  MOE_TRY(check_bias(expert_bias));
+  MOE_TRY(need(y, "y"));
+  if (x == y) return fail(MOE_ERR_INVALID_ARG, "y must not alias x");
+  const size_t need_bytes = layout(shape, false, false).total;
+  if (need_bytes > kNoAllocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "T = %lld needs %zu bytes of intermediates; the static scratch buffer holds %zu (use moe_forward "
+                "with a workspace)",
+                static_cast<long long>(shape->T), need_bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
+  return forward_impl(shape, x, w_gate, bias, w1, w3, w2, expert_bias, y, nullptr, nullptr, 0.f, ws,
+                      kNoAllocScratchBytes, stream, false);
 }
 
 moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma, float eps,

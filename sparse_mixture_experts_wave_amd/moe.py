@@ -170,6 +170,25 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tens
     return out
 
 
+def moe_forward_noalloc(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor], w1: torch.Tensor,
+                        w3: torch.Tensor, w2: torch.Tensor, k: int = 2, out: Optional[torch.Tensor] = None,
+                        b1: Optional[torch.Tensor] = None, b3: Optional[torch.Tensor] = None,
+                        b2: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_forward without a workspace: the library's static per-GPU scratch holds
+    the intermediates.  Nothing is allocated when out is given."""
+    x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
+    w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
+    T, d = x.shape
+    E, d_ff, _ = w1.shape
+    shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
+    _lib.check(_lib.load().moe_forward_noalloc(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3),
+                                               _p(w2), eb, _p(out), _stream(x)))
+    return out
+
+
 def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: torch.Tensor,
                       bias: Optional[torch.Tensor], w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                       k: int = 2, workspace: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,

@@ -120,6 +120,25 @@ def test_forward_rejects_aliased_output(lib):
     assert st == _lib.MOE_ERR_INVALID_ARG and b"alias" in lib.moe_last_error()
 
 
+def test_noalloc_forward_host_checks(lib):
+    """moe_forward_noalloc: its 64 MiB static buffer holds 744 Mixtral tokens'
+    intermediates; 745 are refused before any device call, as are an aliased
+    output and NULL weights.  T = 0 is a no-op."""
+    y = ctypes.c_void_p(0x20000)
+    st = lib.moe_forward_noalloc(ctypes.byref(shape(T=745)), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, y, None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and b"static scratch" in lib.moe_last_error()
+    st = lib.moe_forward_noalloc(ctypes.byref(shape(T=16)), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"alias" in lib.moe_last_error()
+    st = lib.moe_forward_noalloc(ctypes.byref(shape(T=16)), FAKE, FAKE, None, None, FAKE, FAKE, None, y, None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and b"w1 is NULL" in lib.moe_last_error()
+    assert lib.moe_forward_noalloc(ctypes.byref(shape(T=0)), FAKE, FAKE, None, FAKE, FAKE, FAKE, None, y,
+                                   None) == _lib.MOE_OK
+    # the limit: 744 tokens' routing, permutation, h and y_sorted fit 64 MiB, 745 do not
+    per = lambda T: sum(-(-n // 256) * 256 for n in (8 * T, 8 * T, 36, 8 * T, 8 * T, 2 * T * 14336 * 2,
+                                                       2 * T * 4096 * 4))
+    assert per(744) <= 64 << 20 < per(745)
+
+
 def test_expert_bias_pointers_are_validated(lib):
     s = shape(T=16)
     bad = _lib.MoEExpertBias(None, MISALIGNED, None)
