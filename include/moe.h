@@ -194,7 +194,9 @@ moe_status moe_forward_noalloc(const moe_shape* shape, const void* x, const floa
  * * gamma), in place on h:
  *   h_inout [T][d] in act, overwritten with h + MoE(RMSNorm(h))
  *   gamma   [d] fp32;  eps > 0
- * The router sees the fp32 normalised row; the experts see it rounded to act. */
+ * The router's logits are rinv * sum_j (h_j gamma_j) W[e][j] with rinv the fp32
+ * inverse root of the fp32 mean square (the normalised row before rounding);
+ * the experts see the normalised row rounded to act. */
 moe_status moe_block_forward(const moe_shape* shape, void* h_inout, const float* gamma,
                              float eps, const float* w_gate, const float* bias,
                              const void* w1, const void* w3, const void* w2,

@@ -9,9 +9,13 @@ Every function restates, in plain numpy, a passage of the pages it cites
 (page title + section / equation).  Results the pages fix (parameter counts,
 closed forms, invariants) pin it in ``tests/test_oracle_pins.py``.
 
-Parity unpinned: the bf16 output values of the full layer have no external
-vector; they are checked only through the invariants and special cases
-listed in the pin tests (identity case, 28-pair brute force, fp64 shadow).
+Every function is pinned to something other than itself: the whole layer
+(both its token-loop and expert-loop forms) to HuggingFace's
+MixtralSparseMoeBlock in float64, the load-balancing loss to HF's
+load_balancing_loss_func, RoPE and the GQA attention to HF's
+MixtralRotaryEmbedding / MixtralAttention after the pages' q/k row
+permutation, plus the invariants and brute-force cases listed in the pin
+tests (identity case, 28-pair brute force, fp64 shadow, parameter counts).
 """
 from .moe_ref import (  # noqa: F401
     aux_loss_ref,

@@ -600,3 +600,59 @@ def test_planted_topk_P_fails_hf_pin(monkeypatch):
     v = np.array([3.0, 2.0, 0.5, 0.1, -0.2, -1.0, -1.5, -2.0])
     u = np.stack([np.roll(v, s) for s in range(8)])
     assert abs(_mut_stats_topk_P([u], 8, 2)[1].sum() - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# the whole layer against HuggingFace's MixtralSparseMoeBlock ("Mixtral" page,
+# "Загрузка весов HuggingFace": w1 / w3 / w2 map to gate / up / down, and the
+# page's library reproduces HF's logits).  HF computes the softmax over all E
+# logits, keeps the top k and renormalises them: the same weights as a
+# softmax over the kept logits.
+# ---------------------------------------------------------------------------
+def _hf_moe_block(x, wg, w1, w3, w2, k):
+    from transformers import MixtralConfig
+    from transformers.models.mixtral import modeling_mixtral as mm
+
+    E, d_ff, d = w1.shape
+    cfg = MixtralConfig(hidden_size=d, intermediate_size=d_ff, num_local_experts=E, num_experts_per_tok=k)
+    blk = mm.MixtralSparseMoeBlock(cfg).double().eval()
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    with torch.no_grad():
+        blk.gate.weight.copy_(t(wg))
+        blk.experts.gate_up_proj.copy_(torch.cat([t(w1), t(w3)], dim=1))
+        blk.experts.down_proj.copy_(t(w2))
+        return blk(t(x)[None])[0].numpy()
+
+
+@pytest.mark.parametrize("E,k,T,d,d_ff", [(8, 2, 40, 16, 24), (16, 2, 33, 32, 16), (8, 4, 20, 16, 32),
+                                           (4, 1, 25, 8, 16)])
+def test_layer_matches_hf_mixtral_sparse_moe_block(E, k, T, d, d_ff):
+    rng = np.random.default_rng(E * 100 + k)
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((E, d)) * 0.5
+    w1 = rng.standard_normal((E, d_ff, d)) / np.sqrt(d)
+    w3 = rng.standard_normal((E, d_ff, d)) / np.sqrt(d)
+    w2 = rng.standard_normal((E, d, d_ff)) / np.sqrt(d_ff)
+    want = _hf_moe_block(x, wg, w1, w3, w2, k)
+    g = x @ wg.T
+    s = np.sort(g, axis=1)[:, ::-1]
+    clear = (s[:, k - 1] - s[:, k]) > 1e-6 if k < E else np.ones(T, bool)
+    assert clear.mean() > 0.9
+    # HF takes the router softmax in float32 even in a float64 module: weights
+    # carry about 2^-24 of relative error, the rest is float64.
+    for fn in (oracle.moe_forward_expert_loop, oracle.moe_forward_token_loop):
+        got, _ = fn(x, wg, None, w1, w3, w2, k=k, dtype=np.float64)
+        assert np.max(np.abs(got[clear] - want[clear])) <= 1e-6 * np.max(np.abs(want))
+
+
+def test_planted_gate_up_swap_fails_hf_pin(monkeypatch):
+    monkeypatch.setattr(moe_ref, "expert_swiglu", _mut_swap_gate_up)
+    rng = np.random.default_rng(5)
+    T, d, d_ff, E = 30, 16, 24, 8
+    x, wg = rng.standard_normal((T, d)), rng.standard_normal((E, d)) * 0.5
+    w1, w3 = rng.standard_normal((E, d_ff, d)) / 4, rng.standard_normal((E, d_ff, d)) / 4
+    w2 = rng.standard_normal((E, d, d_ff)) / 5
+    got, _ = moe_ref.moe_forward_expert_loop(x, wg, None, w1, w3, w2, dtype=np.float64)
+    monkeypatch.undo()
+    want = _hf_moe_block(x, wg, w1, w3, w2, 2)
+    assert np.max(np.abs(got - want)) > 1e-2 * np.max(np.abs(want))
