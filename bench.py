@@ -443,42 +443,120 @@ def roofline(res):
             "kernel_ms": round(pk[dom], 4)}
 
 
-def cpu_baseline(res, max_tokens: int, budget_s: float = 10.0):
-    """The CPU oracle (expert-loop form, numpy fp32) on a bounded sample of the
-    same workload, on this host's cores: tokens/s."""
-    import numpy as np
+def _host_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS numpy calls."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        import numpy as np
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name', '?')} {dep.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001
+        pass
+    return model, blas
 
-    import oracle
 
-    def host(t):
-        if t is None:
-            return None
-        import torch
-        if t.dtype == torch.bfloat16:
-            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        return t.cpu().numpy()
-
-    cfg, dv = res["cfg"], res["inputs"]
-    n = min(cfg.T, max_tokens)
-    x = host(dv["x"][:n])
-    args = (x, host(dv["w_gate"]), host(dv["bias"]), host(dv["w1"]), host(dv["w3"]), host(dv["w2"]))
+def _blas_threads():
     try:
         import threadpoolctl
-        threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+        return max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
     except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
-    print(f"[bench] cpu oracle on {n} tokens of {cfg.name}", file=sys.stderr, flush=True)
-    oracle.moe_forward_expert_loop(*args)  # warm-up
+        return len(os.sched_getaffinity(0))
+
+
+def _time_runs(fn, budget_s, min_runs=3, max_runs=50):
+    """1 warm-up, then at least min_runs timed runs and more while within budget_s."""
+    fn()
     times = []
     start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - start < budget_s and len(times) < 50):
+    while len(times) < min_runs or (time.perf_counter() - start < budget_s and len(times) < max_runs):
         t0 = time.perf_counter()
-        oracle.moe_forward_expert_loop(*args)
+        fn()
         times.append(time.perf_counter() - t0)
-    med = statistics.median(times)
-    return {"value": round(n / med, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} tokens of {cfg.name} (numpy fp32 expert-loop oracle, weights widened from bf16 "
-                      f"inside), 1 warm-up + {len(times)} timed runs ({sum(times):.1f} s), median {med:.3f} s"}
+    return statistics.median(times), times
+
+
+def _host(t):
+    import numpy as np
+    import torch
+
+    if t is None:
+        return None
+    if t.dtype == torch.bfloat16:
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _oracle_leg(name, cfg, dv, n, budget_s, min_runs=3):
+    """The expert-loop oracle (numpy fp32, BLAS sgemm per expert) on the first n
+    tokens of a workload's inputs."""
+    import oracle
+
+    args = (_host(dv["x"][:n]), _host(dv["w_gate"]), _host(dv["bias"]), _host(dv["w1"]), _host(dv["w3"]),
+            _host(dv["w2"]))
+    print(f"[bench] cpu oracle on {n} tokens of {cfg.name}", file=sys.stderr, flush=True)
+    med, times = _time_runs(lambda: oracle.moe_forward_expert_loop(*args), budget_s, min_runs)
+    flops = 6 * cfg.k * n * cfg.d * cfg.d_ff + 2 * n * cfg.d * cfg.E
+    return {"leg": name, "workload": cfg.name, "tokens": n, "tokens_per_s": round(n / med, 3),
+            "gflops": round(flops / med / 1e9, 2), "median_s": round(med, 4), "runs": len(times),
+            "seconds": round(sum(times), 1)}
+
+
+def cpu_baseline(res, max_tokens: int, budget_s: float = 10.0, prefill_tokens: int = 256):
+    """The CPU oracle on this host's cores, on bounded samples of the workloads.
+
+    The reported value is the expert-loop oracle (numpy fp32) on the decode
+    workload's tokens (tokens/s); further legs: the same oracle on the first
+    prefill_tokens tokens of the prefill workload at full width, and the
+    token-loop form (the definition, single BLAS thread) on the tiny fp32
+    workload.  Each leg: 1 warm-up, then timed runs for about budget_s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth import CONFIGS, generate, generate_torch
+
+    threads = _blas_threads()
+    model, blas = _host_info()
+    cfg, dv = res["cfg"], res["inputs"]
+    legs = [_oracle_leg("expert-loop oracle, decode", cfg, dv, min(cfg.T, max_tokens), budget_s)]
+    pcfg = CONFIGS["mixtral_prefill_t4096"]
+    pdv = generate_torch(pcfg, torch.device("cuda"))
+    legs.append(_oracle_leg("expert-loop oracle, prefill sample", pcfg, pdv, min(pcfg.T, prefill_tokens),
+                            budget_s))
+    del pdv
+    torch.cuda.empty_cache()
+    tcfg = CONFIGS["tiny_fp32"]
+    tin = generate(tcfg)
+    targs = (tin["x"], tin["w_gate"], tin["bias"], tin["w1"], tin["w3"], tin["w2"])
+    print(f"[bench] cpu token-loop oracle on {tcfg.name}", file=sys.stderr, flush=True)
+    try:
+        import threadpoolctl
+        limit = threadpoolctl.threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        limit = None
+    med, times = _time_runs(lambda: oracle.moe_forward_token_loop(*targs), min(budget_s, 3.0))
+    if limit is not None:
+        limit.unregister()
+    tflops = 6 * tcfg.k * tcfg.T * tcfg.d * tcfg.d_ff + 2 * tcfg.T * tcfg.d * tcfg.E
+    legs.append({"leg": "token-loop oracle (the definition), 1 thread", "workload": tcfg.name, "tokens": tcfg.T,
+                 "tokens_per_s": round(tcfg.T / med, 1), "gflops": round(tflops / med / 1e9, 3),
+                 "median_s": round(med, 5), "runs": len(times), "seconds": round(sum(times), 1)})
+    d0 = legs[0]
+    return {"value": d0["tokens_per_s"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "gflops": d0["gflops"], "cpu_model": model, "blas": blas,
+            "sample": f"{d0['tokens']} tokens of {cfg.name} (numpy fp32 expert-loop oracle, weights widened from "
+                      f"bf16 inside), 1 warm-up + {d0['runs']} timed runs ({d0['seconds']} s), median "
+                      f"{d0['median_s']} s; more legs under 'legs'",
+            "legs": legs}
 
 
 def summarize(res):
