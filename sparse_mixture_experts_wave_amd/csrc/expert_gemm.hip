@@ -45,8 +45,13 @@
 // their products land in rows / columns the epilogue never stores.
 //
 // Tile order.  Consecutive tile numbers walk one expert in groups of 8 column
-// tiles x all of its row tiles, so blocks that share a weight tile (or an
-// activation tile) are numbered together.
+// tiles x 4 row tiles, row tile by row tile within a group, so blocks that
+// share a weight tile (or an activation tile) are numbered together.
+// Workgroups go to the 8 XCDs (each with its own L2) in turn, so an XCD gets
+// one column of each group: while a round of 256 runs, each XCD holds 8 weight
+// tiles and 4 activation tiles, each used 4 and 8 times.  (Groups of all of a
+// large expert's row tiles would give an XCD one weight tile and 32 activation
+// tiles, fetched again by every XCD and every column group.)
 //
 // The last round.  A workgroup fills a CU (all of its LDS), so tiles run in
 // rounds of one per CU; when the tile count is not a multiple of the CU count
@@ -68,6 +73,7 @@ constexpr int BK = 32;     // K per LDS slice
 constexpr int NS = 5;      // LDS ring depth (slices)
 constexpr int NTHR = 512;  // 8 waves
 constexpr int NGROUP = 8;  // column tiles per tile-order group
+constexpr int RBLOCK = 4;  // row tiles per tile-order group
 constexpr int SLICE = BM * BK;  // elements per operand slice
 constexpr int COPIES = 4;       // copy instructions per thread per slice
 constexpr int MAX_SPLIT = 8;    // K pieces per split tile
@@ -126,11 +132,14 @@ __device__ __forceinline__ bool map_tile(const int32_t* __restrict__ offsets, in
     const int cnt = mt * NT;
     if (L < cum + cnt) {
       const int i = L - cum;
-      const int g = i / (mt * NGROUP);
-      const int gi = i - g * mt * NGROUP;
+      const int rb = i / (RBLOCK * NT);          // row block (the last may be short)
+      const int rbr = min(RBLOCK, mt - rb * RBLOCK);
+      const int ib = i - rb * RBLOCK * NT;
+      const int g = ib / (rbr * NGROUP);
+      const int gi = ib - g * rbr * NGROUP;
       const int gw = min(NGROUP, NT - g * NGROUP);
-      const int m = gi / gw;
-      const int nn = gi - m * gw;
+      const int m = rb * RBLOCK + gi / gw;
+      const int nn = gi - (gi / gw) * gw;
       t.e = e;
       t.m0 = lo + m * BM;
       t.rows = min(BM, n_e - m * BM);
