@@ -32,6 +32,11 @@
 // memory phases, into the slots of slices that were read at least one
 // interval before, and each wave waits for its own copies of slice s+1
 // (s_waitcnt vmcnt) just before the barrier that opens it.
+// The main loop runs ten slices per trip and each wave group its own copy of
+// it, so every step's ring slot, copy parity and LDS destinations are
+// compile-time constants; copies past the last slice re-copy the last one
+// into a slot no wave still reads, which keeps every wait count constant
+// (about 5 % faster than runtime slot parity and guarded copies).
 //
 // LDS layout: a slice is [256 rows][32] bf16, 64 bytes per row; row r keeps
 // its four 16-byte chunks at position c ^ ((r >> 2) & 3), so the 16
@@ -223,29 +228,32 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 struct CopySrc {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t off[COPIES];
+  int last;  // the last K slice of the tile (or piece)
+  int woff;  // element offset of the wave's first row (64 (w & 3)) in a slot
 };
 
-// One copy: row group j (rows 64 (w & 3) + 16 j + lane / 4) of K slice s
-// into ring slot B (group 0 copies A, group 1 copies B).
-template <int B>
+// One copy: row group j (rows 64 (w & 3) + 16 j + lane / 4) of K slice s into
+// ring slot B; group 0 copies A, group 1 copies B (GRP is the wave's group).
+// A slice past the last one is copied as the last one: the schedule stays the
+// same to the end, and such a copy lands in the slot of a slice every wave
+// has finished with.
+template <int B, int GRP>
 __device__ __forceinline__ void copy_one(const CopySrc& cs, int s, int j) {
-  const int wave = threadIdx.x >> 6;
-  uint16_t* ring = (wave >> 2) == 0 ? ring_a<B>() : ring_b<B>();
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(cs.rsrc, (lds_ptr)(ring + ((wave & 3) * 64 + j * 16) * BK), 16,
-                                           cs.off[j] + s * (BK * 2), 0, 0, 0);
+  uint16_t* ring = GRP == 0 ? ring_a<B>() : ring_b<B>();
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(cs.rsrc, (lds_ptr)(ring + cs.woff + j * 16 * BK), 16,
+                                           cs.off[j] + min(s, cs.last) * (BK * 2), 0, 0, 0);
 }
 
 // Slices 2m and 2m+1 hold the two 64-byte halves of the same 128-byte row
 // segments, so their copies go out in pairs, back to back per row group:
 // the second copy of a pair reads lines the first has just brought in.  Row
-// groups j0, j0+1 of the pair (s0, s0+1) into slots SA, SB; slices past KT
-// are skipped.
-template <int SA, int SB>
-__device__ __forceinline__ void copy_pair_half(const CopySrc& cs, int s0, int j0, int KT) {
+// groups j0, j0+1 of the pair (s0, s0+1) into slots SA, SB.
+template <int SA, int SB, int GRP>
+__device__ __forceinline__ void copy_pair_half(const CopySrc& cs, int s0, int j0) {
 #pragma unroll
   for (int j = j0; j < j0 + 2; ++j) {
-    if (s0 < KT) copy_one<SA>(cs, s0, j);
-    if (s0 + 1 < KT) copy_one<SB>(cs, s0 + 1, j);
+    copy_one<SA, GRP>(cs, s0, j);
+    copy_one<SB, GRP>(cs, s0 + 1, j);
   }
 }
 
@@ -253,71 +261,93 @@ __device__ __forceinline__ void copy_pair_half(const CopySrc& cs, int s0, int j0
 // of the pair (s+3, s+4); that of an even slice s copies row groups 2, 3 of
 // the pair (s+2, s+3).  Before the barrier that opens slice s+1, each wave
 // waits for its own copies of s+1: 5 younger copies may stay in flight after
-// an odd slice, 8 after an even one (fewer near the end: wait for all).
-__device__ __forceinline__ void wait_slice_next(int s, int KT) {
-  if (s & 1) {
-    if (s + 4 < KT) wait_vmcnt<5>();
-    else wait_vmcnt<0>();
-  } else {
-    if (s + 3 < KT) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
-  }
+// an odd slice, 8 after an even one.
+template <bool ODD>
+__device__ __forceinline__ void wait_slice_next() {
+  if constexpr (ODD) wait_vmcnt<5>();
+  else wait_vmcnt<8>();
 }
 
-// One K slice s (ring slot B = s % NS), as two intervals: memory phase
-// (operand reads of slice s, half a pair of copies) and compute phase (16
-// MFMAs).  Group 1 runs each phase one interval after group 0.
-template <bool GATED, bool FULL, int B>
-__device__ __forceinline__ void slice_step(const CopySrc& cs, int s, int KT, int grp, const bool (&live)[4],
-                                           f32x16 (&acc)[4][2]) {
+// One K slice s (ring slot B = s % NS, ODD = s & 1, both fixed at compile
+// time), as two intervals: memory phase (operand reads of slice s, half a
+// pair of copies) and compute phase (16 MFMAs).  Group 1 runs each phase one
+// interval after group 0.
+template <bool GATED, bool FULL, int GRP, int B, bool ODD>
+__device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[4], f32x16 (&acc)[4][2]) {
   Frag f0, f1;
   read_frag<GATED>(ring_a<B>(), ring_b<B>(), 0, f0);
   read_frag<GATED>(ring_a<B>(), ring_b<B>(), 1, f1);
-  if (s & 1)
-    copy_pair_half<(B + 3) % NS, (B + 4) % NS>(cs, s + 3, 0, KT);
+  if constexpr (ODD)
+    copy_pair_half<(B + 3) % NS, (B + 4) % NS, GRP>(cs, s + 3, 0);
   else
-    copy_pair_half<(B + 2) % NS, (B + 3) % NS>(cs, s + 2, 2, KT);
+    copy_pair_half<(B + 2) % NS, (B + 3) % NS, GRP>(cs, s + 2, 2);
   wait_lgkm0();
-  if (grp == 1) wait_slice_next(s, KT);
+  if constexpr (GRP == 1) wait_slice_next<ODD>();
   bar();
   mma<FULL>(f0, live, acc);
   mma<FULL>(f1, live, acc);
-  if (grp == 0) wait_slice_next(s, KT);
+  if constexpr (GRP == 0) wait_slice_next<ODD>();
   bar();
 }
 
-template <bool GATED, bool FULL>
-__device__ __forceinline__ void mainloop(const CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
-  const int wave = threadIdx.x >> 6;
-  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
+template <bool GATED, bool FULL, int GRP>
+__device__ __forceinline__ void mainloop_grp(CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
   bool live[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) live[mi] = FULL || (grp * 128 + mi * 32 < rows);
+  for (int mi = 0; mi < 4; ++mi) live[mi] = FULL || (GRP * 128 + mi * 32 < rows);
 
-  const int KT = K / BK;  // >= 2 (K is a multiple of 64)
+  const int KT = K / BK;  // >= 2 and even (K is a multiple of 64)
+  cs.last = KT - 1;
   // Prologue: slices 0 and 1 whole, row groups 0, 1 of slices 2 and 3.
-  copy_pair_half<0, 1>(cs, 0, 0, KT);
-  copy_pair_half<0, 1>(cs, 0, 2, KT);
-  copy_pair_half<2, 3>(cs, 2, 0, KT);
-  if (KT >= 4)
-    wait_vmcnt<5>();  // slice 0's last copy is followed by 5
-  else
-    wait_vmcnt<0>();
+  copy_pair_half<0, 1, GRP>(cs, 0, 0);
+  copy_pair_half<0, 1, GRP>(cs, 0, 2);
+  copy_pair_half<2, 3, GRP>(cs, 2, 0);
+  wait_vmcnt<5>();  // slice 0's last copy is followed by 5
   bar();
-  if (grp == 1) bar_group1_start();
+  if constexpr (GRP == 1) bar_group1_start();
+  // Ten slices per trip, so that each step's ring slot and parity are fixed.
   int s = 0;
-  for (; s + NS <= KT; s += NS) {
-    slice_step<GATED, FULL, 0>(cs, s, KT, grp, live, acc);
-    slice_step<GATED, FULL, 1>(cs, s + 1, KT, grp, live, acc);
-    slice_step<GATED, FULL, 2>(cs, s + 2, KT, grp, live, acc);
-    slice_step<GATED, FULL, 3>(cs, s + 3, KT, grp, live, acc);
-    slice_step<GATED, FULL, 4>(cs, s + 4, KT, grp, live, acc);
+  for (; s + 2 * NS <= KT; s += 2 * NS) {
+    slice_step<GATED, FULL, GRP, 0, false>(cs, s, live, acc);
+    slice_step<GATED, FULL, GRP, 1, true>(cs, s + 1, live, acc);
+    slice_step<GATED, FULL, GRP, 2, false>(cs, s + 2, live, acc);
+    slice_step<GATED, FULL, GRP, 3, true>(cs, s + 3, live, acc);
+    slice_step<GATED, FULL, GRP, 4, false>(cs, s + 4, live, acc);
+    slice_step<GATED, FULL, GRP, 0, true>(cs, s + 5, live, acc);
+    slice_step<GATED, FULL, GRP, 1, false>(cs, s + 6, live, acc);
+    slice_step<GATED, FULL, GRP, 2, true>(cs, s + 7, live, acc);
+    slice_step<GATED, FULL, GRP, 3, false>(cs, s + 8, live, acc);
+    slice_step<GATED, FULL, GRP, 4, true>(cs, s + 9, live, acc);
   }
-  if (s < KT) slice_step<GATED, FULL, 0>(cs, s, KT, grp, live, acc);
-  if (s + 1 < KT) slice_step<GATED, FULL, 1>(cs, s + 1, KT, grp, live, acc);
-  if (s + 2 < KT) slice_step<GATED, FULL, 2>(cs, s + 2, KT, grp, live, acc);
-  if (s + 3 < KT) slice_step<GATED, FULL, 3>(cs, s + 3, KT, grp, live, acc);
-  if (grp == 0) bar_group0_end();  // same barrier count for both groups
+  // The rest: an even number of slices below ten (s is a multiple of 10).
+  if (s < KT) {
+    slice_step<GATED, FULL, GRP, 0, false>(cs, s, live, acc);
+    slice_step<GATED, FULL, GRP, 1, true>(cs, s + 1, live, acc);
+  }
+  if (s + 2 < KT) {
+    slice_step<GATED, FULL, GRP, 2, false>(cs, s + 2, live, acc);
+    slice_step<GATED, FULL, GRP, 3, true>(cs, s + 3, live, acc);
+  }
+  if (s + 4 < KT) {
+    slice_step<GATED, FULL, GRP, 4, false>(cs, s + 4, live, acc);
+    slice_step<GATED, FULL, GRP, 0, true>(cs, s + 5, live, acc);
+  }
+  if (s + 6 < KT) {
+    slice_step<GATED, FULL, GRP, 1, false>(cs, s + 6, live, acc);
+    slice_step<GATED, FULL, GRP, 2, true>(cs, s + 7, live, acc);
+  }
+  if constexpr (GRP == 0) bar_group0_end();  // same barrier count for both groups
+  wait_vmcnt<0>();  // the copies issued past the last slice, before anything reuses the LDS
+}
+
+template <bool GATED, bool FULL>
+__device__ __forceinline__ void mainloop(CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  cs.woff = (wave & 3) * 64 * BK;
+  if (wave < 4)
+    mainloop_grp<GATED, FULL, 0>(cs, K, rows, acc);
+  else
+    mainloop_grp<GATED, FULL, 1>(cs, K, rows, acc);
 }
 
 // Number of tiles (sum over experts of the row tiles, times NT).
