@@ -10,8 +10,15 @@
 // (rows of one expert) x (weight rows).  For the up projection the 256 weight
 // rows are 128 rows of W1 and the same 128 rows of W3, so SiLU(gate) * up is
 // formed in registers and only h is written.  The eight waves sit 2 (rows) x 4
-// (columns); each computes 128 x 64 with v_mfma_f32_32x32x16_bf16 (4 x 2
-// blocks of 32x32, 128 fp32 accumulators per lane).
+// (columns); each computes 128 x 64 with v_mfma_f32_16x16x32_bf16 (8 x 4
+// blocks of 16x16, one MFMA per block and 32-wide K slice, 128 fp32
+// accumulators per lane).  Under sustained load the chip is power-limited,
+// and 16x16x32 MFMAs run at a higher clock than 32x32x16 ones for the same
+// work (all CUs, random bf16 operands: 2.02-2.05 against 1.73-1.80 GHz).  In
+// this kernel that raises the clock from 1.53 to 1.72 GHz but the matrix
+// cores then wait more (busy 0.64 against 0.73): the tile's throughput is set
+// by the global -> LDS copies, not by the MFMA rate; the 16x16 blocks cost
+// fewer registers and speed up the down projection a little.
 //
 // Ping-pong schedule.  Waves 0-3 (group 0) and 4-7 (group 1) put one wave of
 // each group on every SIMD, and the groups run half a step apart: while one
@@ -156,36 +163,42 @@ __device__ __forceinline__ bool map_tile(const int32_t* __restrict__ offsets, in
   return false;
 }
 
-// Operands of one 16-wide k-step: four 32-row A slices and two 32-row B slices.
+// Operands of one 32-wide K slice: eight 16-row A blocks and four 16-row B
+// blocks.  With v_mfma_f32_16x16x32_bf16, lane (r = lane % 16, c = lane / 16)
+// holds the 16-byte chunk c (k = 8c .. 8c+7) of row r of each block.
 struct Frag {
-  bf16x8 a[4], b[2];
+  bf16x8 a[8], b[4];
 };
 
+// Weight row (within the tile) of B block nb's row r.  Gated: blocks 0, 1 are
+// W1 rows (gate) and 2, 3 the same rows of W3 (up).
 template <bool GATED>
-__device__ __forceinline__ void read_frag(const uint16_t* As, const uint16_t* Bs, int kk, Frag& f) {
+__device__ __forceinline__ int b_row(int wn, int nb, int r) {
+  return (GATED ? (nb >> 1) * 128 + wn * 32 + (nb & 1) * 16 : wn * 64 + nb * 16) + r;
+}
+
+template <bool GATED>
+__device__ __forceinline__ void read_frag(const uint16_t* As, const uint16_t* Bs, Frag& f) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2;
   const int wn = wave & 3;
-  const int c = 2 * kk + (lane >> 5);
+  const int c = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) f.a[mi] = as_bf16x8(load16(As + swz(wm * 128 + mi * 32 + (lane & 31), c)));
+  for (int mi = 0; mi < 8; ++mi) f.a[mi] = as_bf16x8(load16(As + swz(wm * 128 + mi * 16 + r, c)));
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = (GATED ? nb * 128 + wn * 32 : wn * 64 + nb * 32) + (lane & 31);
-    f.b[nb] = as_bf16x8(load16(Bs + swz(r, c)));
-  }
+  for (int nb = 0; nb < 4; ++nb) f.b[nb] = as_bf16x8(load16(Bs + swz(b_row<GATED>(wn, nb, r), c)));
 }
 
-// FULL: every 32-row slice of the tile holds rows; otherwise slices past
+// FULL: every 16-row block of the tile is multiplied; otherwise blocks past
 // the last row (a wave-uniform test) skip their MFMAs.
 template <bool FULL>
-__device__ __forceinline__ void mma(const Frag& f, const bool (&live)[4], f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void mma(const Frag& f, const bool (&live)[8], f32x4 (&acc)[8][4]) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      if (FULL || live[mi]) acc[mi][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mi], f.b[nb], acc[mi][nb], 0, 0, 0);
+    for (int nb = 0; nb < 4; ++nb)
+      if (FULL || live[mi]) acc[mi][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[mi], f.b[nb], acc[mi][nb], 0, 0, 0);
 }
 
 // The LDS ring: NS slices of A and of B, each a distinct array, so that the
@@ -273,10 +286,9 @@ __device__ __forceinline__ void wait_slice_next() {
 // pair of copies) and compute phase (16 MFMAs).  Group 1 runs each phase one
 // interval after group 0.
 template <bool GATED, bool FULL, int GRP, int B, bool ODD>
-__device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[4], f32x16 (&acc)[4][2]) {
-  Frag f0, f1;
-  read_frag<GATED>(ring_a<B>(), ring_b<B>(), 0, f0);
-  read_frag<GATED>(ring_a<B>(), ring_b<B>(), 1, f1);
+__device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[8], f32x4 (&acc)[8][4]) {
+  Frag f;
+  read_frag<GATED>(ring_a<B>(), ring_b<B>(), f);
   if constexpr (ODD)
     copy_pair_half<(B + 3) % NS, (B + 4) % NS, GRP>(cs, s + 3, 0);
   else
@@ -284,17 +296,16 @@ __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool 
   wait_lgkm0();
   if constexpr (GRP == 1) wait_slice_next<ODD>();
   bar();
-  mma<FULL>(f0, live, acc);
-  mma<FULL>(f1, live, acc);
+  mma<FULL>(f, live, acc);
   if constexpr (GRP == 0) wait_slice_next<ODD>();
   bar();
 }
 
 template <bool GATED, bool FULL, int GRP>
-__device__ __forceinline__ void mainloop_grp(CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
-  bool live[4];
+__device__ __forceinline__ void mainloop_grp(CopySrc& cs, int K, int rows, f32x4 (&acc)[8][4]) {
+  bool live[8];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) live[mi] = FULL || (GRP * 128 + mi * 32 < rows);
+  for (int mi = 0; mi < 8; ++mi) live[mi] = FULL || (GRP * 128 + mi * 16 < rows);
 
   const int KT = K / BK;  // >= 2 and even (K is a multiple of 64)
   cs.last = KT - 1;
@@ -341,7 +352,7 @@ __device__ __forceinline__ void mainloop_grp(CopySrc& cs, int K, int rows, f32x1
 }
 
 template <bool GATED, bool FULL>
-__device__ __forceinline__ void mainloop(CopySrc& cs, int K, int rows, f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void mainloop(CopySrc& cs, int K, int rows, f32x4 (&acc)[8][4]) {
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   cs.woff = (wave & 3) * 64 * BK;
   if (wave < 4)
@@ -398,16 +409,17 @@ __device__ __forceinline__ float swap_pair(float y) {
 }
 
 // Epilogue of one tile: biases, then SiLU(gate) * up rounded to bf16 (up) or
-// fp32 (down).  32x32 accumulator layout: lane holds column lane%32 and rows
-// 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block.  Gated: the W1 and W3
-// bias of the lane's one column.
-// Only the 32-row blocks mi in [mlo, mhi) of each wave are stored.  With
-// resid set (not gated) the fp32 result is not stored: it is added to the bf16
-// matrix resid in place with one rounding, resid = bf16(resid + (acc + bias)),
-// the residual connection after an output projection.  With ro.q set (not
-// gated) the result goes to q, k, v as RopeOut describes.
+// fp32 (down).  16x16 accumulator layout: lane holds column lane%16 and rows
+// 4*(lane/16) + v of each 16x16 block.  Gated: blocks nb and nb + 2 hold the
+// gate and up sums of the same output column.
+// Only the rows of 32-row blocks [mlo, mhi) of each wave (16-row blocks
+// [2 mlo, 2 mhi)) are stored.  With resid set (not gated) the fp32 result is
+// not stored: it is added to the bf16 matrix resid in place with one
+// rounding, resid = bf16(resid + (acc + bias)), the residual connection after
+// an output projection.  With ro.q set (not gated) the result goes to q, k, v
+// as RopeOut describes.
 template <bool GATED>
-__device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4][2],
+__device__ __forceinline__ void store_tile(const Tile& t, const f32x4 (&acc)[8][4],
                                            const uint16_t* __restrict__ bias0,
                                            const uint16_t* __restrict__ bias1, void* __restrict__ out,
                                            uint16_t* __restrict__ resid, const RopeOut& ro, int N,
@@ -416,11 +428,14 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 2;
   const int wn = wave & 3;
-  float bb[2];
+  const int lc = lane & 15, lr = 4 * (lane >> 4);  // the lane's column and first row in a block
+  // Output column of block nb (gated: of blocks nb and nb + 2).
+  auto col = [&](int nb) { return GATED ? t.n0 + wn * 32 + (nb & 1) * 16 + lc : t.n0 + wn * 64 + nb * 16 + lc; };
+  float bb[4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = GATED ? t.n0 + wn * 32 + (lane & 31) : t.n0 + wn * 64 + nb * 32 + (lane & 31);
-    const uint16_t* bsrc = (GATED && nb == 1) ? bias1 : bias0;
+  for (int nb = 0; nb < 4; ++nb) {
+    const int n = col(nb);
+    const uint16_t* bsrc = (GATED && nb >= 2) ? bias1 : bias0;
     bb[nb] = (bsrc && n < N) ? bf16_to_f32(bsrc[static_cast<int64_t>(t.e) * N + n]) : 0.f;
   }
   if constexpr (!GATED) {
@@ -438,27 +453,27 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
         dst = ro.k, ld = ro.nkv, c0 = nw - ro.nq, rot = true;
       }
       const bool odd = lane & 1;
-      const int i0 = ((c0 & 127) + (lane & 31)) >> 1;  // pair index of column nb = 0; nb = 1 adds 16
+      const int i0 = ((c0 & 127) + lc) >> 1;  // pair index of block nb = 0; block nb adds 8 nb
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < mlo || mi >= mhi) continue;
+      for (int mi = 0; mi < 8; ++mi) {
+        if (mi < 2 * mlo || mi >= 2 * mhi) continue;
         // The block's angles first (rows clamped into the tile, as for the
         // residual loads), so that their loads overlap.
-        float2 cs[16][2];
+        float2 cs[4][4];
         if (rot) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
+          for (int v = 0; v < 4; ++v)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              const int r = min(wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), t.rows - 1);
-              cs[v][nb] = ro.cs[static_cast<int64_t>(t.m0 + r) * 64 + i0 + 16 * nb];
+            for (int nb = 0; nb < 4; ++nb) {
+              const int r = min(wm * 128 + mi * 16 + lr + v, t.rows - 1);
+              cs[v][nb] = ro.cs[static_cast<int64_t>(t.m0 + r) * 64 + i0 + 8 * nb];
             }
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          for (int nb = 0; nb < 4; ++nb) {
+            const int r = wm * 128 + mi * 16 + lr + v;
             float y = acc[mi][nb][v] + bb[nb];
             if (rot) {
               // Both lanes of a pair hold the same row, so they take this
@@ -468,34 +483,34 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
               const float c = cs[v][nb].x, sn = cs[v][nb].y;
               y = odd ? x0 * sn + x1 * c : x0 * c - x1 * sn;
             }
-            if (r < t.rows) dst[static_cast<int64_t>(t.m0 + r) * ld + c0 + nb * 32 + (lane & 31)] = f32_to_bf16(y);
+            if (r < t.rows) dst[static_cast<int64_t>(t.m0 + r) * ld + c0 + nb * 16 + lc] = f32_to_bf16(y);
           }
       }
       return;
     }
     if (resid) {
-      // Per 32-row block: every residual load is issued before the first
+      // Per 16-row block: every residual load is issued before the first
       // store, so their latencies overlap.  The loads are unconditional (rows
       // and columns past the tile's edge are clamped to its last valid one)
       // so that no branch forces a wait between them.
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < mlo || mi >= mhi) continue;
-        uint16_t hv[16][2];
+      for (int mi = 0; mi < 8; ++mi) {
+        if (mi < 2 * mlo || mi >= 2 * mhi) continue;
+        uint16_t hv[4][4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int r = min(wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), t.rows - 1);
-            const int n = min(t.n0 + wn * 64 + nb * 32 + (lane & 31), N - 1);
+          for (int nb = 0; nb < 4; ++nb) {
+            const int r = min(wm * 128 + mi * 16 + lr + v, t.rows - 1);
+            const int n = min(col(nb), N - 1);
             hv[v][nb] = resid[static_cast<int64_t>(t.m0 + r) * N + n];
           }
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
+        for (int v = 0; v < 4; ++v)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
+          for (int nb = 0; nb < 4; ++nb) {
+            const int r = wm * 128 + mi * 16 + lr + v;
+            const int n = col(nb);
             if (r < t.rows && n < N)
               resid[static_cast<int64_t>(t.m0 + r) * N + n] =
                   f32_to_bf16(bf16_to_f32(hv[v][nb]) + (acc[mi][nb][v] + bb[nb]));
@@ -505,39 +520,39 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[4]
     }
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (mi < mlo || mi >= mhi || r >= t.rows) continue;
+    for (int v = 0; v < 4; ++v) {
+      const int r = wm * 128 + mi * 16 + lr + v;
+      if (mi < 2 * mlo || mi >= 2 * mhi || r >= t.rows) continue;
       const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
       if constexpr (GATED) {
-        const int n = t.n0 + wn * 32 + (lane & 31);
-        if (n < N)
-          static_cast<uint16_t*>(out)[row + n] = f32_to_bf16(silu_fast(acc[mi][0][v] + bb[0]) * (acc[mi][1][v] + bb[1]));
-      } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int n = t.n0 + wn * 64 + nb * 32 + (lane & 31);
+          const int n = col(nb);
+          if (n < N)
+            static_cast<uint16_t*>(out)[row + n] =
+                f32_to_bf16(silu_fast(acc[mi][nb][v] + bb[nb]) * (acc[mi][nb + 2][v] + bb[nb + 2]));
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int n = col(nb);
           if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v] + bb[nb];
         }
       }
     }
 }
 
-// A thread's 128 accumulators as 32 float4 chunks, chunk c of thread i at
-// part[c * NTHR + i] of its piece: each chunk store is one coalesced 8 KiB.
-__device__ __forceinline__ void store_partial(float4* __restrict__ part, const f32x16 (&acc)[4][2]) {
+// A thread's 128 accumulators as 32 float4 chunks (chunk 4 mi + nb is block
+// (mi, nb)), chunk c of thread i at part[c * NTHR + i] of its piece: each
+// chunk store is one coalesced 8 KiB.
+__device__ __forceinline__ void store_partial(float4* __restrict__ part, const f32x4 (&acc)[8][4]) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = (mi * 2 + nb) * 4 + j;
-        part[c * NTHR + threadIdx.x] =
-            make_float4(acc[mi][nb][4 * j], acc[mi][nb][4 * j + 1], acc[mi][nb][4 * j + 2], acc[mi][nb][4 * j + 3]);
-      }
+    for (int nb = 0; nb < 4; ++nb)
+      part[(mi * 4 + nb) * NTHR + threadIdx.x] = make_float4(acc[mi][nb][0], acc[mi][nb][1], acc[mi][nb][2], acc[mi][nb][3]);
 }
 
 template <bool GATED>
@@ -608,16 +623,17 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
     Kp = (s1 - s0) * BK;
   }
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[mi][nb][v] = 0.f;
 
-  // Every 32-row slice holds at least one row once rows > BM - 32: the
-  // branch-free path then does the same MFMAs.
+  // Every 32-row block holds at least one row once rows > BM - 32: the
+  // branch-free path then does all MFMAs (at most one 16-row block of them
+  // on clamped rows, whose results are not stored).
   if (t.rows > BM - 32)
     mainloop<GATED, true>(cs, Kp, t.rows, acc);
   else
@@ -647,28 +663,26 @@ __global__ __launch_bounds__(NTHR) void gemm_fixup_kernel(const int32_t* __restr
   Tile t;
   if (!map_tile(offsets, E, NT, COLS, plan.full + b, t)) return;
   if (mb * 32 >= t.rows) return;  // no valid row in this block of either wave row
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[mi][nb][v] = 0.f;
+      for (int v = 0; v < 4; ++v) acc[mi][nb][v] = 0.f;
   for (int p = 0; p < plan.S; ++p) {
     const float4* src = part + (static_cast<int64_t>(b) * plan.S + p) * ACC_CHUNKS * NTHR;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      if (mi != mb) continue;
+    for (int mi = 0; mi < 8; ++mi) {
+      if ((mi >> 1) != mb) continue;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 v = src[((mi * 2 + nb) * 4 + j) * NTHR + threadIdx.x];
-          acc[mi][nb][4 * j] += v.x;
-          acc[mi][nb][4 * j + 1] += v.y;
-          acc[mi][nb][4 * j + 2] += v.z;
-          acc[mi][nb][4 * j + 3] += v.w;
-        }
+      for (int nb = 0; nb < 4; ++nb) {
+        const float4 v = src[(mi * 4 + nb) * NTHR + threadIdx.x];
+        acc[mi][nb][0] += v.x;
+        acc[mi][nb][1] += v.y;
+        acc[mi][nb][2] += v.z;
+        acc[mi][nb][3] += v.w;
+      }
     }
   }
   store_tile<GATED>(t, acc, bias0, bias1, out, resid, ro, N, mb, mb + 1);
