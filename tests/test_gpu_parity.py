@@ -194,6 +194,9 @@ def test_combine_residual_may_alias_output():
     (64, 512, 1024, "bf16", "stream"),
     (65, 512, 1024, "bf16", "gemm"),  # one token past the streaming limit, same widths
     (16, 192, 256, "bf16", "gemm"),   # d not a multiple of 512: small T on the GEMM path
+    (100, 64, 64, "bf16", "gemm"),    # K = 64: two 32-wide slices, the shortest main loop
+    (200, 128, 128, "bf16", "gemm"),  # four slices: no ten-slice trip, two tail pairs
+    (130, 64, 832, "bf16", "gemm"),   # up: 2 slices; down: 26 = 20 + 6; d_ff not a multiple of 128
 ])
 def test_expert_ffn(T, d, d_ff, dtype, path):
     say(f"expert_ffn T={T} d={d} d_ff={d_ff} {dtype} {path}")
