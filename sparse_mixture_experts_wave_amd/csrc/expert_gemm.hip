@@ -22,7 +22,7 @@
 //
 // Ping-pong schedule.  Waves 0-3 (group 0) and 4-7 (group 1) put one wave of
 // each group on every SIMD, and the groups run half a step apart: while one
-// group issues the 16 MFMAs of a 32-wide K slice, the other reads its next
+// group issues the 32 MFMAs of a 32-wide K slice, the other reads its next
 // slice's operands from LDS and issues its share of the global -> LDS copies.
 // Every such interval ends in a barrier of all eight waves, so the matrix core
 // of each SIMD always has one wave feeding it.  Group 0 copies the A slices,
@@ -52,7 +52,7 @@
 // contiguously; each lane picks the global chunk that belongs at its slot.
 //
 // Ragged expert tails.  Row tiles are numbered per expert (ceil(n_e / 256)
-// each); a tile's 32-row slices past the expert's last row skip their MFMAs.
+// each); a tile's 16-row blocks past the expert's last row skip their MFMAs.
 // Rows past the last one (and weight rows past N) are clamped to valid rows:
 // their products land in rows / columns the epilogue never stores.
 //
@@ -283,7 +283,7 @@ __device__ __forceinline__ void wait_slice_next() {
 
 // One K slice s (ring slot B = s % NS, ODD = s & 1, both fixed at compile
 // time), as two intervals: memory phase (operand reads of slice s, half a
-// pair of copies) and compute phase (16 MFMAs).  Group 1 runs each phase one
+// pair of copies) and compute phase (32 MFMAs).  Group 1 runs each phase one
 // interval after group 0.
 template <bool GATED, bool FULL, int GRP, int B, bool ODD>
 __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[8], f32x4 (&acc)[8][4]) {
