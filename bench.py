@@ -81,9 +81,35 @@ def _elapsed_ms(hip, a, b) -> float:
     return float(ms.value)
 
 
+def _code_only(text: str) -> str:
+    """The source with comments removed (string and character literals kept)
+    and runs of whitespace collapsed: what the compiler sees."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def _src_sha(name: str) -> str:
+    """Hash of a kernel source file's code (comments and layout ignored), so
+    that counter entries stay valid across comment edits."""
     path = os.path.join(ROOT, "sparse_mixture_experts_wave_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    return hashlib.sha256(_code_only(open(path, encoding="utf-8").read()).encode()).hexdigest()[:16]
 
 
 def _traffic(workload: str, kernel: str, T: int):
