@@ -348,7 +348,7 @@ __device__ __forceinline__ void mainloop_grp(CopySrc& cs, int K, int rows, f32x4
     slice_step<GATED, FULL, GRP, 2, true>(cs, s + 7, live, acc);
   }
   if constexpr (GRP == 0) bar_group0_end();  // same barrier count for both groups
-  wait_vmcnt<0>();  // the copies issued past the last slice, before anything reuses the LDS
+  wait_vmcnt<0>();  // the copies issued past the last slice land before the workgroup's LDS is released
 }
 
 template <bool GATED, bool FULL>
