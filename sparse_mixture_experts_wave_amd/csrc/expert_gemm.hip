@@ -587,7 +587,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
   // rows of h are contiguous, so the descriptor starts at the tile).  Group 1:
   // the tile's weight rows of W1 (waves 4, 5) or W3 (waves 6, 7) in the up
   // projection, of W2 in the down projection.  Every offset stays below 4 GiB:
-  // the host requires T*d and d*d_ff below 2^31 elements.
+  // a gathered row index is below T and the host requires T*d below 2^31
+  // elements; every other descriptor starts at the tile's first row and
+  // covers at most 256 rows of K elements.
   CopySrc cs;
   const uint16_t* base;
   if (wave < 4) {
