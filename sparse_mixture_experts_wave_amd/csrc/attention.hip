@@ -157,8 +157,8 @@ __global__ void row_range_kernel(int32_t* __restrict__ offsets, int32_t rows) {
 // operand straight from registers, the MFMA's k order taken to be the order in
 // which the S^T accumulator holds the keys; V is staged transposed in LDS.
 // The softmax is rescaled lazily: the reference max moves only when a tile's
-// max exceeds it by more than 8 (log2 units).  Heads of one K/V group are
-// adjacent in the grid, the longest query tiles first.
+// max exceeds it by more than 8 (log2 units).  The heads of one K/V group run
+// on one XCD, the longest query tiles first.
 //
 // Software pipelining.  Per tile j a wave runs, in order:
 //   A: S(j+1) for keys 0..31 of tile j+1 (8 MFMAs) beside tile j's row max;
@@ -222,7 +222,12 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BKV * FA_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][FA_D * VT_STRIDE];
 
-  const int h = blockIdx.x;
+  // Workgroups go to the 8 XCDs in turn by linear id, and gridDim.x = H: with
+  // H a multiple of 8, XCD x gets heads x H/8 .. x H/8 + H/8 - 1, so the heads
+  // that share a K/V group read it through one XCD's L2 (with the heads of a
+  // group on different XCDs each L2 fetched K and V again: 2.8x the HBM reads).
+  const int h = (H % 8 == 0) ? static_cast<int>(blockIdx.x % 8) * (H / 8) + static_cast<int>(blockIdx.x / 8)
+                             : static_cast<int>(blockIdx.x);
   const int n_qt = (T + FA_BQ - 1) / FA_BQ;
   const int q0 = (n_qt - 1 - static_cast<int>(blockIdx.y)) * FA_BQ;  // longest rows first
   const int g = h / (H / G);
@@ -343,8 +348,12 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   auto tile = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int kv0 = j * FA_BKV;
     const int buf = j & 1;
-    if (j + 2 < ntiles) load_k(kv0 + 2 * FA_BKV);
-    if (j + 1 < ntiles) load_v(kv0 + FA_BKV);
+    // Loads and stores run on every tile, past the last one too: their key
+    // rows are clamped to T - 1, and such a store lands in a buffer that
+    // nothing reads again but the S of a tile past the end.  Guarded loads made the compiler
+    // wait for each tile's K loads before it issued the V loads.
+    load_k(kv0 + 2 * FA_BKV);
+    load_v(kv0 + FA_BKV);
     if (kv0 <= qw + FA_QW - 1) {  // some key of tile j is visible to some query of the wave
       if (kv0 + FA_BKV - 1 > qw) {  // causal mask on the diagonal tiles only
 #pragma unroll
@@ -387,8 +396,8 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       o_half(buf, 1, pw1);
       l += lt + __shfl_xor(lt, 32);
     }
-    if (j + 2 < ntiles) store_k(buf);
-    if (j + 1 < ntiles) store_v(buf ^ 1);
+    store_k(buf);
+    store_v(buf ^ 1);
     __syncthreads();
   };
 
