@@ -350,8 +350,9 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int buf = j & 1;
     // Loads and stores run on every tile, past the last one too: their key
     // rows are clamped to T - 1, and such a store lands in a buffer that
-    // nothing reads again but the S of a tile past the end.  Guarded loads made the compiler
-    // wait for each tile's K loads before it issued the V loads.
+    // nothing reads again but the S of a tile past the end.  Guarded loads
+    // made the compiler wait for each tile's K loads before it issued the V
+    // loads.
     load_k(kv0 + 2 * FA_BKV);
     load_v(kv0 + FA_BKV);
     if (kv0 <= qw + FA_QW - 1) {  // some key of tile j is visible to some query of the wave
