@@ -25,6 +25,8 @@ def _gpu():
 
 @pytest.mark.parametrize("T,H,G", [
     (1, 4, 2), (2, 8, 8), (64, 4, 1), (100, 8, 2), (129, 4, 4), (300, 8, 1), (1000, 32, 8), (2048, 8, 2),
+    # heads dealt to the 8 XCDs in runs of H/8: groups of 4 heads over 2 XCDs, groups of 8 over 3
+    (700, 16, 4), (384, 24, 3),
 ])
 def test_gqa_attention_core(T, H, G):
     say(f"gqa core T={T} H={H} G={G}")
