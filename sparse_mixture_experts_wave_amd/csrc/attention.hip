@@ -266,19 +266,28 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   static_assert(FA_KC == 2, "two K chunks per thread");
   const int kg = tid & 31, dg = tid >> 5;
   const uint32_t ld_kv32 = static_cast<uint32_t>(ld_kv);
-  const uint16_t* kbase = k + g * FA_D + ((FA_KC * tid) & 15) * 8;
-  const uint16_t* vbase = v + g * FA_D + 8 * dg;
+  // Buffer loads through one descriptor per K and V head group, with 32-bit
+  // byte offsets (below 2^32: the launcher rejects T * G * d_h >= 2^31): no
+  // 64-bit address arithmetic per load (2 % of the kernel against global
+  // loads).
+  const __amdgpu_buffer_rsrc_t krs = wave_rsrc(k + g * FA_D);
+  const __amdgpu_buffer_rsrc_t vrs = wave_rsrc(v + g * FA_D);
+  const uint32_t kchunk = ((FA_KC * tid) & 15) * 16;  // bytes
+  const uint32_t vchunk = 16 * dg;
+  const uint32_t row_bytes = 2 * ld_kv32;
   const int vcol = vt_col(2 * kg);
   u32x4 kr[FA_KC], vr[2];
   auto load_k = [&](int kv0) {
-    const uint32_t ro = __umul24(static_cast<uint32_t>(min(kv0 + (tid >> 3), T - 1)), ld_kv32);
-    kr[0] = load16(kbase + ro);
-    kr[1] = load16(kbase + ro + 8);
+    const uint32_t ro = __umul24(static_cast<uint32_t>(min(kv0 + (tid >> 3), T - 1)), row_bytes) + kchunk;
+    kr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ro, 0, 0));
+    kr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, ro + 16, 0, 0));
   };
   auto load_v = [&](int kv0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      vr[i] = load16(vbase + __umul24(static_cast<uint32_t>(min(kv0 + 2 * kg + i, T - 1)), ld_kv32));
+      vr[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     vrs, __umul24(static_cast<uint32_t>(min(kv0 + 2 * kg + i, T - 1)), row_bytes) + vchunk, 0, 0));
   };
   auto store_k = [&](int buf) {
 #pragma unroll
