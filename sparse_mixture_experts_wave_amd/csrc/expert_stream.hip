@@ -245,8 +245,8 @@ hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, cons
   // Few tokens touch few experts (up to about 7 at T = 8): narrower work
   // items (16 columns) keep every workgroup busy; the K split doubles when it
   // divides evenly.
-  if (T <= 8 && d % 1024 == 0)
-    return launch_mb<1, 8, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
+  if (T <= 8 && d % 1024 == 0)  // at most 8 rows per expert: one 16-row M-block
+    return launch_cfg<1, 1, 8, true>(x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
   return launch_mb<2, 4, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
 }
 
@@ -257,9 +257,9 @@ hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, co
   // With 1-8 tokens only 2-7 experts are touched: an 8-way K split keeps
   // enough loads in flight when it divides evenly (at T = 8 it takes the
   // layer from 399 to 386 us).
-  if (T <= 8 && d_ff % 1024 == 0)
-    return launch_mb<1, 8, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
-  if (T <= 4) return launch_mb<1, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
+  if (T <= 8 && d_ff % 1024 == 0)  // one 16-row M-block, as above
+    return launch_cfg<1, 1, 8, false>(h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
+  if (T <= 4) return launch_cfg<1, 1, 4, false>(h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
   return launch_mb<2, 4, false>(T, h, nullptr, offsets, p, d, d_ff, E, kStreamGrid, stream);
 }
 
