@@ -400,7 +400,7 @@ def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: 
 
     # A short timed region straight after the GPU went idle reads high by a
     # fixed start-up cost (measured: the sublayer at 0.57-0.59 ms over 10
-    # calls against 0.53 ms over 30, same box), so each timing warms up for
+    # calls against 0.53 ms over 30 on the same GPU), so each timing warms up for
     # about 20 ms of work and times at least 30 calls (10 decoder layers).
     def timed(fn, n):
         t0 = time.perf_counter()
