@@ -72,6 +72,47 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+# The C ABI sees only pointers: the layouts include/moe.h states are checked
+# here, so that a mis-shaped or mis-typed tensor raises instead of being read
+# or written past its end.
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+
+
+def _rows(t: torch.Tensor, name: str, dtype: torch.dtype, rows: int, cols: Optional[int] = None) -> None:
+    """t must hold at least `rows` rows (of `cols` columns when given) of dtype."""
+    ok = t.dtype == dtype and t.dim() == (1 if cols is None else 2) and t.shape[0] >= rows
+    if ok and cols is not None:
+        ok = t.shape[1] == cols
+    if not ok:
+        want = f"[>= {rows}]" if cols is None else f"[>= {rows}, {cols}]"
+        raise ValueError(f"{name} must be {dtype} {want}, got {t.dtype} {list(t.shape)}")
+
+
+def _activations(x: torch.Tensor, name: str = "x"):
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be [T, d], got {list(x.shape)}")
+    return x.shape
+
+
+def _layer_weights(d: int, w_gate: Optional[torch.Tensor], bias: Optional[torch.Tensor], w1: torch.Tensor,
+                   w3: torch.Tensor, w2: torch.Tensor):
+    """Router (fp32 [E, d], bias fp32 [E]) and expert weights (w1, w3 [E, d_ff, d], w2 [E, d, d_ff], one
+    dtype) against the activation width d -> (E, d_ff)."""
+    if w1.dim() != 3:
+        raise ValueError(f"w1 must be [E, d_ff, d], got {list(w1.shape)}")
+    E, d_ff, _ = w1.shape
+    _need(w1, "w1", w1.dtype, (E, d_ff, d))
+    _need(w3, "w3", w1.dtype, (E, d_ff, d))
+    _need(w2, "w2", w1.dtype, (E, d, d_ff))
+    if w_gate is not None:
+        _need(w_gate, "w_gate", torch.float32, (E, d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    return E, d_ff
+
+
 # d_ff does not enter the router, dispatch or combine; any valid value does.
 _D_FF_UNUSED = 64
 
@@ -80,10 +121,11 @@ def moe_route(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor
               want_logits: bool = False) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
     """Router logits -> (topk_idx [T,k] int32, topk_w [T,k] fp32, logits [T,E] fp32 or None)."""
     x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
-    T, d = x.shape
+    T, d = _activations(x)
     E = w_gate.shape[0]
-    if w_gate.dtype != torch.float32 or tuple(w_gate.shape) != (E, d):
-        raise ValueError("w_gate must be float32 [E, d]")
+    _need(w_gate, "w_gate", torch.float32, (E, d))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
     shape = make_shape(T, d, _D_FF_UNUSED, E, k, x.dtype)
     idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
@@ -96,8 +138,8 @@ def moe_route(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tensor
 def moe_dispatch(topk_idx: torch.Tensor, E: int, d: int = 64):
     """-> (expert_offsets [E+1], sorted_token [T*k], inv_pos [T,k]) int32."""
     topk_idx = _gpu(topk_idx, "topk_idx")
-    if topk_idx.dtype != torch.int32:
-        raise ValueError("topk_idx must be int32")
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2:
+        raise ValueError(f"topk_idx must be int32 [T, k], got {topk_idx.dtype} {list(topk_idx.shape)}")
     T, k = topk_idx.shape
     shape = make_shape(T, d, _D_FF_UNUSED, E, k, torch.bfloat16)
     dev = topk_idx.device
@@ -117,13 +159,15 @@ def moe_expert_ffn(x: torch.Tensor, expert_offsets: torch.Tensor, sorted_token: 
 
     b1, b3 [E, d_ff] and b2 [E, d] are the experts' optional Linear biases."""
     x, w1, w3, w2 = _gpu(x, "x"), _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
-    T, d = x.shape
-    E, d_ff, _ = w1.shape
-    if tuple(w1.shape) != (E, d_ff, d) or tuple(w3.shape) != (E, d_ff, d) or tuple(w2.shape) != (E, d, d_ff):
-        raise ValueError("expert weights must be w1, w3 [E, d_ff, d] and w2 [E, d, d_ff]")
+    expert_offsets, sorted_token = _gpu(expert_offsets, "expert_offsets"), _gpu(sorted_token, "sorted_token")
+    T, d = _activations(x)
+    E, d_ff = _layer_weights(d, None, None, w1, w3, w2)
+    _need(expert_offsets, "expert_offsets", torch.int32, (E + 1,))
+    _rows(sorted_token, "sorted_token", torch.int32, T * k)
     shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
     if y_sorted is None:
         y_sorted = torch.empty((max(T * k, 1), d), dtype=torch.float32, device=x.device)
+    _rows(_gpu(y_sorted, "y_sorted"), "y_sorted", torch.float32, T * k, d)
     ws = _ws(expert_ffn_workspace_size(shape), x.device)
     eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
     _lib.check(_lib.load().moe_expert_ffn(ctypes.byref(shape), _p(x), _p(expert_offsets), _p(sorted_token),
@@ -138,11 +182,19 @@ def moe_combine(y_sorted: torch.Tensor, inv_pos: torch.Tensor, topk_w: torch.Ten
     """y[t] = sum_s w[t,s] * y_sorted[inv_pos[t,s]] (+ residual[t]) -> [T, d] in out_dtype."""
     y_sorted, inv_pos, topk_w = _gpu(y_sorted, "y_sorted"), _gpu(inv_pos, "inv_pos"), _gpu(topk_w, "topk_w")
     residual = _gpu(residual, "residual")
+    if inv_pos.dim() != 2 or y_sorted.dim() != 2:
+        raise ValueError("inv_pos must be [T, k] and y_sorted [rows, d]")
     T, k = inv_pos.shape
     d = y_sorted.shape[1]
+    _need(inv_pos, "inv_pos", torch.int32, (T, k))
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _rows(y_sorted, "y_sorted", torch.float32, T * k, d)
+    if residual is not None:
+        _need(residual, "residual", out_dtype, (T, d))
     shape = make_shape(T, d, _D_FF_UNUSED, E, k, out_dtype)
     if out is None:
         out = torch.empty((T, d), dtype=out_dtype, device=y_sorted.device)
+    _need(_gpu(out, "out"), "out", out_dtype, (T, d))
     _lib.check(_lib.load().moe_combine(ctypes.byref(shape), _p(y_sorted), _p(inv_pos), _p(topk_w), _p(residual),
                                        _p(out), _stream(y_sorted)))
     return out
@@ -157,11 +209,12 @@ def moe_forward(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[torch.Tens
     bias is the router's; b1, b3 [E, d_ff] and b2 [E, d] the experts' optional Linear biases."""
     x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
     w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
-    T, d = x.shape
-    E, d_ff, _ = w1.shape
+    T, d = _activations(x)
+    E, d_ff = _layer_weights(d, w_gate, bias, w1, w3, w2)
     shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
     if out is None:
         out = torch.empty_like(x)
+    _need(_gpu(out, "out"), "out", x.dtype, (T, d))
     if workspace is None:
         workspace = _ws(workspace_size(shape), x.device)
     eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
@@ -178,11 +231,12 @@ def moe_forward_noalloc(x: torch.Tensor, w_gate: torch.Tensor, bias: Optional[to
     the intermediates.  Nothing is allocated when out is given."""
     x, w_gate, bias = _gpu(x, "x"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
     w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
-    T, d = x.shape
-    E, d_ff, _ = w1.shape
+    T, d = _activations(x)
+    E, d_ff = _layer_weights(d, w_gate, bias, w1, w3, w2)
     shape = make_shape(T, d, d_ff, E, k, x.dtype, w1.dtype)
     if out is None:
         out = torch.empty_like(x)
+    _need(_gpu(out, "out"), "out", x.dtype, (T, d))
     eb = _expert_bias(b1, b3, b2, E, d, d_ff, w1.dtype)
     _lib.check(_lib.load().moe_forward_noalloc(ctypes.byref(shape), _p(x), _p(w_gate), _p(bias), _p(w1), _p(w3),
                                                _p(w2), eb, _p(out), _stream(x)))
@@ -196,8 +250,9 @@ def moe_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float, w_gate: 
     """In place: h <- h + MoE(RMSNorm(h) * gamma).  Returns h."""
     h, gamma, w_gate, bias = _gpu(h, "h"), _gpu(gamma, "gamma"), _gpu(w_gate, "w_gate"), _gpu(bias, "bias")
     w1, w3, w2 = _gpu(w1, "w1"), _gpu(w3, "w3"), _gpu(w2, "w2")
-    T, d = h.shape
-    E, d_ff, _ = w1.shape
+    T, d = _activations(h, "h")
+    E, d_ff = _layer_weights(d, w_gate, bias, w1, w3, w2)
+    _need(gamma, "gamma", torch.float32, (d,))
     shape = make_shape(T, d, d_ff, E, k, h.dtype, w1.dtype)
     if workspace is None:
         workspace = _ws(workspace_size(shape), h.device)
@@ -251,9 +306,12 @@ def moe_gqa_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d: Opti
     G = k.shape[1]
     if tuple(k.shape) != (T, G, dh) or tuple(v.shape) != (T, G, dh):
         raise ValueError("k and v must be [T, G, d_h] with q [T, H, d_h]")
+    if v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
     shape = make_attn_shape(T, d if d is not None else H * dh, H, G, dh, q.dtype)
     if out is None:
         out = torch.empty_like(q)
+    _need(_gpu(out, "out"), "out", q.dtype, (T, H, dh))
     _lib.check(_lib.load().moe_gqa_attention(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(out), _stream(q)))
     return out
 
@@ -265,10 +323,13 @@ def moe_attention_block_forward(h: torch.Tensor, gamma: torch.Tensor, eps: float
 
     wqkv is [(H + 2G) d_h, d]: W_Q rows, then W_K, then W_V; wo is [d, H d_h]."""
     h, gamma, wqkv, wo = _gpu(h, "h"), _gpu(gamma, "gamma"), _gpu(wqkv, "wqkv"), _gpu(wo, "wo")
-    T, d = h.shape
+    T, d = _activations(h, "h")
+    if wo.dim() != 2 or H < 1 or wo.shape[1] % H != 0:
+        raise ValueError(f"wo must be [d, H d_h], got {list(wo.shape)} with H = {H}")
     dh = wo.shape[1] // H
-    if tuple(wqkv.shape) != ((H + 2 * G) * dh, d) or tuple(wo.shape) != (d, H * dh):
-        raise ValueError("wqkv must be [(H + 2G) d_h, d] and wo [d, H d_h]")
+    _need(wqkv, "wqkv", h.dtype, ((H + 2 * G) * dh, d))
+    _need(wo, "wo", h.dtype, (d, H * dh))
+    _need(gamma, "gamma", torch.float32, (d,))
     shape = make_attn_shape(T, d, H, G, dh, h.dtype)
     if workspace is None:
         workspace = _ws(attention_workspace_size(shape), h.device)

@@ -7,8 +7,9 @@ import shutil
 import subprocess
 
 import pytest
+import torch
 
-from sparse_mixture_experts_wave_amd import _lib
+from sparse_mixture_experts_wave_amd import _lib, moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
@@ -245,3 +246,58 @@ def test_c99_client_compiles_links_and_runs(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
     assert "k = 9 rejected" in run.stdout
+
+
+# ---------------------------------------------------------------------------
+# the binding's layout checks (host logic on CPU tensors: the C ABI sees only
+# pointers, so a mis-shaped tensor must be refused before any call)
+# ---------------------------------------------------------------------------
+def _weights(E=4, d=64, d_ff=128, dt=torch.bfloat16):
+    return (torch.zeros(E, d, dtype=torch.float32), torch.zeros(E, dtype=torch.float32),
+            torch.zeros(E, d_ff, d, dtype=dt), torch.zeros(E, d_ff, d, dtype=dt), torch.zeros(E, d, d_ff, dtype=dt))
+
+
+def test_binding_accepts_the_stated_layouts():
+    w_gate, bias, w1, w3, w2 = _weights()
+    assert moe._layer_weights(64, w_gate, bias, w1, w3, w2) == (4, 128)
+    assert moe._layer_weights(64, None, None, w1, w3, w2) == (4, 128)
+    moe._rows(torch.zeros(10, dtype=torch.int32), "st", torch.int32, 10)
+    moe._rows(torch.zeros(12, 64, dtype=torch.float32), "ys", torch.float32, 10, 64)
+
+
+@pytest.mark.parametrize("bad", ["w_gate_bf16", "w_gate_rows", "bias_len", "w3_shape", "w2_transposed",
+                                 "w2_dtype", "w1_2d", "width"])
+def test_binding_refuses_mis_shaped_weights(bad):
+    w_gate, bias, w1, w3, w2 = _weights()
+    d = 64
+    if bad == "w_gate_bf16":
+        w_gate = w_gate.to(torch.bfloat16)
+    elif bad == "w_gate_rows":
+        w_gate = torch.zeros(8, 64, dtype=torch.float32)
+    elif bad == "bias_len":
+        bias = torch.zeros(8, dtype=torch.float32)
+    elif bad == "w3_shape":
+        w3 = torch.zeros(4, 64, 64, dtype=torch.bfloat16)
+    elif bad == "w2_transposed":
+        w2 = torch.zeros(4, 128, 64, dtype=torch.bfloat16)
+    elif bad == "w2_dtype":
+        w2 = w2.to(torch.float32)
+    elif bad == "w1_2d":
+        w1 = torch.zeros(4 * 128, 64, dtype=torch.bfloat16)
+    elif bad == "width":
+        d = 128
+    with pytest.raises(ValueError):
+        moe._layer_weights(d, w_gate, bias, w1, w3, w2)
+
+
+def test_binding_refuses_short_row_buffers():
+    with pytest.raises(ValueError):
+        moe._rows(torch.zeros(9, dtype=torch.int32), "sorted_token", torch.int32, 10)
+    with pytest.raises(ValueError):
+        moe._rows(torch.zeros(10, 32, dtype=torch.float32), "y_sorted", torch.float32, 10, 64)
+    with pytest.raises(ValueError):
+        moe._rows(torch.zeros(10, 64, dtype=torch.bfloat16), "y_sorted", torch.float32, 10, 64)
+    with pytest.raises(ValueError):
+        moe._need(torch.zeros(16, 64, dtype=torch.float32), "out", torch.bfloat16, (16, 64))
+    with pytest.raises(ValueError):
+        moe._activations(torch.zeros(2, 16, 64))
