@@ -22,7 +22,9 @@ the C ABI); the roofline fraction is that of the dominant kernel.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes
+import gc
 import hashlib
 import json
 import os
@@ -197,6 +199,19 @@ def work_model(cfg, counts):
     }
 
 
+@contextlib.contextmanager
+def _no_gc():
+    """No Python garbage collection inside a timed region: a collection pass
+    stalls the launching thread, and a region of a few milliseconds would
+    count that stall as GPU time."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
 def measure(cfg, steps: int, warmup: int):
     """Time `steps` steps of the workload: one moe_forward call, or for a stack
     workload one moe_block_forward call per layer on a resident residual stream."""
@@ -238,27 +253,29 @@ def measure(cfg, steps: int, warmup: int):
 
     # Timed region 1: K steps exactly as a caller runs them -> value.
     print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    plain_ms = (time.perf_counter() - t0) * 1e3 / steps
+    with _no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        plain_ms = (time.perf_counter() - t0) * 1e3 / steps
 
     # Timed region 2: the same K steps with the C ABI timing points recording
     # HIP events on the launch stream between kernels -> per-kernel durations.
     npts = _lib.MOE_TIMING_POINTS
     evs = [[[_event(hip) for _ in range(npts)] for _ in layers] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        for j, lw in enumerate(layers):
-            arr = (ctypes.c_void_p * npts)(*[e.value for e in evs[i][j]])
-            _lib.check(lib.moe_set_timing_events(arr, npts))
-            call(lw)
-    _lib.check(lib.moe_set_timing_events(None, 0))
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    with _no_gc():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            for j, lw in enumerate(layers):
+                arr = (ctypes.c_void_p * npts)(*[e.value for e in evs[i][j]])
+                _lib.check(lib.moe_set_timing_events(arr, npts))
+                call(lw)
+        _lib.check(lib.moe_set_timing_events(None, 0))
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     calls = [e for per_step in evs for e in per_step]
     per_kernel = {name: statistics.fmean(_elapsed_ms(hip, e[j], e[j + 1]) for e in calls)
                   for j, name in enumerate(KERNELS)}
@@ -300,12 +317,13 @@ def measure_decode_latency(steps: int, Ts=(1, 2, 4, 8, 16)):
         args = (x, dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
         for _ in range(3):
             moe.moe_forward(*args, out=y, workspace=ws)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            moe.moe_forward(*args, out=y, workspace=ws)
-        torch.cuda.synchronize()
-        eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+        with _no_gc():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                moe.moe_forward(*args, out=y, workspace=ws)
+            torch.cuda.synchronize()
+            eager_ms = (time.perf_counter() - t0) * 1e3 / steps
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -316,12 +334,13 @@ def measure_decode_latency(steps: int, Ts=(1, 2, 4, 8, 16)):
             moe.moe_forward(*args, out=y, workspace=ws)
         for _ in range(3):
             g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+        with _no_gc():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - t0) * 1e3 / steps
         idx, _, _ = moe.moe_route(x, dv["w_gate"], dv["bias"])
         off, _, _ = moe.moe_dispatch(idx, cfg.E)
         counts = np.diff(off.cpu().numpy()).tolist()
@@ -409,12 +428,13 @@ def measure_attention(steps: int, T: int = 4096, d: int = 4096, H: int = 32, G: 
         one = time.perf_counter() - t0
         for _ in range(max(1, int(0.02 / max(one, 1e-6)))):
             fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n
+        with _no_gc():
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                fn()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / n
 
     steps = max(30, steps)
     core_ms = timed(lambda: moe.moe_gqa_attention(q, k, v, out=o), steps)
