@@ -101,6 +101,8 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
+// s_waitcnt lgkmcnt(0) (vmcnt, expcnt left unconstrained).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // A barrier that the compiler may move no instruction across, LDS accesses
 // included: the s_barrier builtin is not a memory barrier for the optimizer,
@@ -282,11 +284,18 @@ __device__ __forceinline__ void wait_slice_next() {
 // One K slice s (ring slot B = s % NS, ODD = s & 1, both fixed at compile
 // time), as two intervals: memory phase (operand reads of slice s, half a
 // pair of copies) and compute phase (32 MFMAs).  Group 1 runs each phase one
-// interval after group 0.  The memory phase does not wait for its operand
-// reads: they land in the wave's own registers, the MFMAs wait for each one
-// (lgkmcnt) as they need it, and no copy targets slot B until two intervals
-// later.  (Waiting for all of them before the barrier kept the slower group
-// from the barrier for the reads' whole latency: 3-4 % of the kernel.)
+// interval after group 0.
+//
+// Operand reads land in the wave's own registers and the MFMAs of the next
+// interval wait for each one (lgkmcnt) as they need it, so a memory phase
+// waits for its reads before the barrier only where a copy could target
+// their slot in the very next interval.  The next copy into slot B is that of
+// slice s+5: group 0 issues half of it (rows 0-31 of each wave, A) at its odd
+// step s+1 when s is even, one interval after group 1 has read slice s; every
+// other one comes two or more intervals after the reads, by when the reading
+// wave's own MFMAs have waited for them.  So group 1 waits for its reads at
+// even steps only.  (Waiting in every memory phase kept the group from the
+// barrier for the reads' whole latency: 3-4 % of the kernel.)
 template <bool GATED, bool FULL, int GRP, int B, bool ODD>
 __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[8], f32x4 (&acc)[8][4]) {
   Frag f;
@@ -295,6 +304,7 @@ __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool 
     copy_pair_half<(B + 3) % NS, (B + 4) % NS, GRP>(cs, s + 3, 0);
   else
     copy_pair_half<(B + 2) % NS, (B + 3) % NS, GRP>(cs, s + 2, 2);
+  if constexpr (GRP == 1 && !ODD) wait_lgkm0();
   if constexpr (GRP == 1) wait_slice_next<ODD>();
   bar();
   mma<FULL>(f, live, acc);
