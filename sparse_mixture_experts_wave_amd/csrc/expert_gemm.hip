@@ -101,8 +101,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
-// s_waitcnt lgkmcnt(0) (vmcnt, expcnt left unconstrained).
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt with only an lgkmcnt limit (vmcnt, expcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));
+}
 
 // A barrier that the compiler may move no instruction across, LDS accesses
 // included: the s_barrier builtin is not a memory barrier for the optimizer,
@@ -184,8 +188,19 @@ __device__ __forceinline__ void read_frag(const uint16_t* As, const uint16_t* Bs
   const int wm = wave >> 2;
   const int wn = wave & 3;
   const int c = lane >> 4, r = lane & 15;
+  // A blocks 0, 1, 4, 5 first: they hold rows 0-31 of each wave's 64-row
+  // copy block, the rows a copy may reach one interval later (see slice_step).
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi) f.a[mi] = as_bf16x8(load16(As + swz(wm * 128 + mi * 16 + r, c)));
+  for (int i = 0; i < 4; ++i) {
+    const int mi = (i & 1) + 4 * (i >> 1);
+    f.a[mi] = as_bf16x8(load16(As + swz(wm * 128 + mi * 16 + r, c)));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mi = 2 + (i & 1) + 4 * (i >> 1);
+    f.a[mi] = as_bf16x8(load16(As + swz(wm * 128 + mi * 16 + r, c)));
+  }
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) f.b[nb] = as_bf16x8(load16(Bs + swz(b_row<GATED>(wn, nb, r), c)));
 }
@@ -288,14 +303,16 @@ __device__ __forceinline__ void wait_slice_next() {
 //
 // Operand reads land in the wave's own registers and the MFMAs of the next
 // interval wait for each one (lgkmcnt) as they need it, so a memory phase
-// waits for its reads before the barrier only where a copy could target
-// their slot in the very next interval.  The next copy into slot B is that of
-// slice s+5: group 0 issues half of it (rows 0-31 of each wave, A) at its odd
-// step s+1 when s is even, one interval after group 1 has read slice s; every
-// other one comes two or more intervals after the reads, by when the reading
-// wave's own MFMAs have waited for them.  So group 1 waits for its reads at
-// even steps only.  (Waiting in every memory phase kept the group from the
-// barrier for the reads' whole latency: 3-4 % of the kernel.)
+// waits for its reads before the barrier only where a copy could overwrite
+// them in the very next interval.  The next copy into slot B is that of
+// slice s+5: group 0 issues half of it (A, rows 0-31 of each 64-row copy
+// block) at its odd step s+1 when s is even, one interval after group 1 has
+// read slice s; every other one comes two or more intervals after the reads,
+// by when the reading wave's own MFMAs have waited for them.  So group 1
+// waits at even steps only, and only for its A reads of those rows (blocks
+// 0, 1, 4, 5, issued first: lgkmcnt(8) leaves the other eight reads in
+// flight).  (Waiting for every read in every memory phase kept the group from
+// the barrier for the reads' whole latency: 4-5 % of the kernel.)
 template <bool GATED, bool FULL, int GRP, int B, bool ODD>
 __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool (&live)[8], f32x4 (&acc)[8][4]) {
   Frag f;
@@ -304,7 +321,10 @@ __device__ __forceinline__ void slice_step(const CopySrc& cs, int s, const bool 
     copy_pair_half<(B + 3) % NS, (B + 4) % NS, GRP>(cs, s + 3, 0);
   else
     copy_pair_half<(B + 2) % NS, (B + 3) % NS, GRP>(cs, s + 2, 2);
-  if constexpr (GRP == 1 && !ODD) wait_lgkm0();
+  if constexpr (GRP == 1 && !ODD) {
+    __builtin_amdgcn_sched_barrier(0);  // all twelve reads issued before the count is taken
+    wait_lgkm<8>();                     // the four reads issued first have landed
+  }
   if constexpr (GRP == 1) wait_slice_next<ODD>();
   bar();
   mma<FULL>(f, live, acc);
