@@ -42,12 +42,66 @@ __device__ __forceinline__ void shuffle_rows(u32x4* buf, u32x4 (&v)[4], int lane
   for (int j = 0; j < 4; ++j) v[j] = buf[16 * m + ((4 * j + q) ^ m)];
 }
 
-template <int MB, int NG, int KS, bool GATED>
+// The dispatch of a decode-size layer, done by the up projection itself (no
+// launch of its own): the router's top-k choices in, and the permutation the
+// down projection and the combine read out.
+struct FusedDispatch {
+  const int32_t* topk;  // [pairs] expert of each (token, slot) pair
+  int pairs, k;
+  int32_t* offsets;       // [E + 1]
+  int32_t* sorted_token;  // [pairs]
+  int32_t* inv_pos;       // [pairs]
+};
+constexpr int kFuseMaxPairs = 64;
+constexpr int kFuseMaxE = 64;
+
+// With FUSED every workgroup first sorts the (token, slot) pairs by expert in
+// LDS: the stable counting sort of the dispatch kernel (expert by expert,
+// tokens ascending; "Mixtral" page, "Алгоритм"), at most 64 pairs, and
+// workgroup 0 also stores it for the kernels that follow.
+template <int MB, int NG, int KS, bool GATED, bool FUSED>
 __global__ __launch_bounds__(64 * KS) void stream_ffn_bf16_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ gather,
-    const int32_t* __restrict__ offsets, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ gather_in,
+    const int32_t* __restrict__ offsets_in, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, const uint16_t* __restrict__ bias0,
-    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int E) {
+    const uint16_t* __restrict__ bias1, void* __restrict__ out, int N, int K, int E, FusedDispatch fd) {
+  static_assert(64 * KS > kFuseMaxE, "one thread per expert and per pair");
+  __shared__ int32_t off_s[kFuseMaxE + 1];
+  __shared__ int32_t row_s[kFuseMaxPairs];
+  const int32_t* gather = FUSED ? row_s : gather_in;
+  const int32_t* offsets = FUSED ? off_s : offsets_in;
+  if constexpr (FUSED) {
+    __shared__ int32_t sel[kFuseMaxPairs];
+    const int tid = threadIdx.x;
+    if (tid < fd.pairs) sel[tid] = fd.topk[tid];
+    __syncthreads();
+    if (tid < E) {
+      int c = 0;
+      for (int p = 0; p < fd.pairs; ++p) c += sel[p] == tid;
+      off_s[tid + 1] = c;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      off_s[0] = 0;
+      for (int e = 0; e < E; ++e) off_s[e + 1] += off_s[e];
+    }
+    __syncthreads();
+    if (tid < fd.pairs) {
+      // Row of pair (t, s): its expert's first row plus the earlier tokens
+      // that chose the same expert (a token's k experts are distinct).
+      const int t = tid / fd.k, e = sel[tid];
+      int rank = 0;
+      for (int p = 0; p < t * fd.k; ++p) rank += sel[p] == e;
+      const int pos = off_s[e] + rank;
+      row_s[pos] = t;
+      if (blockIdx.x == 0) {
+        fd.sorted_token[pos] = t;
+        fd.inv_pos[tid] = pos;
+      }
+    }
+    if (blockIdx.x == 0 && tid <= E) fd.offsets[tid] = off_s[tid];
+    __syncthreads();
+  }
   constexpr int NACC = MB * NG * (GATED ? 2 : 1);
   __shared__ f32x4 red[KS - 1][NACC][64];
   // Per-wave staging of one 16-row x 256-byte weight block: row r keeps its
@@ -208,23 +262,23 @@ struct Proj {
   void* out;
 };
 
-template <int MB, int NG, int KS, bool GATED>
+template <int MB, int NG, int KS, bool GATED, bool FUSED = false>
 hipError_t launch_cfg(const uint16_t* A, const int32_t* gather, const int32_t* offsets, const Proj& p, int N,
-                      int K, int E, int grid, hipStream_t s) {
+                      int K, int E, int grid, hipStream_t s, const FusedDispatch& fd = {}) {
   const int items = E * (N / (16 * NG));
   const int blocks = grid > 0 && grid < items ? grid : items;
-  stream_ffn_bf16_kernel<MB, NG, KS, GATED><<<blocks, 64 * KS, 0, s>>>(A, gather, offsets, p.B0, p.B1, p.bias0,
-                                                                        p.bias1, p.out, N, K, E);
+  stream_ffn_bf16_kernel<MB, NG, KS, GATED, FUSED><<<blocks, 64 * KS, 0, s>>>(
+      A, gather, offsets, p.B0, p.B1, p.bias0, p.bias1, p.out, N, K, E, fd);
   return hipGetLastError();
 }
 
-template <int NG, int KS, bool GATED>
+template <int NG, int KS, bool GATED, bool FUSED = false>
 hipError_t launch_mb(int64_t T, const uint16_t* A, const int32_t* gather, const int32_t* offsets, const Proj& p,
-                     int N, int K, int E, int grid, hipStream_t s) {
+                     int N, int K, int E, int grid, hipStream_t s, const FusedDispatch& fd = {}) {
   // n_e <= T: the experts of one token are distinct.
-  if (T <= 16) return launch_cfg<1, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
-  if (T <= 32) return launch_cfg<2, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
-  return launch_cfg<4, NG, KS, GATED>(A, gather, offsets, p, N, K, E, grid, s);
+  if (T <= 16) return launch_cfg<1, NG, KS, GATED, FUSED>(A, gather, offsets, p, N, K, E, grid, s, fd);
+  if (T <= 32) return launch_cfg<2, NG, KS, GATED, FUSED>(A, gather, offsets, p, N, K, E, grid, s, fd);
+  return launch_cfg<4, NG, KS, GATED, FUSED>(A, gather, offsets, p, N, K, E, grid, s, fd);
 }
 
 // Workgroups of the grid-stride loop (8 per CU on 256 CUs): enough bytes in
@@ -248,6 +302,23 @@ hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, cons
   if (T <= 8 && d % 1024 == 0)  // at most 8 rows per expert: one 16-row M-block
     return launch_cfg<1, 1, 8, true>(x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
   return launch_mb<2, 4, true>(T, x, sorted_token, offsets, p, d_ff, d, E, kStreamGrid, stream);
+}
+
+bool stream_dispatch_supported(int64_t T, int k, int d, int d_ff, int E) {
+  return stream_supported(T, d, d_ff) && T * k <= kFuseMaxPairs && E <= kFuseMaxE;
+}
+
+hipError_t launch_stream_up_dispatch_bf16(const uint16_t* x, const int32_t* topk_idx, int k, int32_t* offsets,
+                                          int32_t* sorted_token, int32_t* inv_pos, const uint16_t* w1,
+                                          const uint16_t* w3, const uint16_t* b1, const uint16_t* b3, uint16_t* h,
+                                          int64_t T, int d, int d_ff, int E, hipStream_t stream) {
+  if (!stream_dispatch_supported(T, k, d, d_ff, E)) return hipErrorInvalidValue;
+  const Proj p{w1, w3, b1, b3, h};
+  const FusedDispatch fd{topk_idx, static_cast<int>(T) * k, k, offsets, sorted_token, inv_pos};
+  // The same configurations as launch_stream_up_bf16.
+  if (T <= 8 && d % 1024 == 0)
+    return launch_cfg<1, 1, 8, true, true>(x, nullptr, nullptr, p, d_ff, d, E, kStreamGrid, stream, fd);
+  return launch_mb<2, 4, true, true>(T, x, nullptr, nullptr, p, d_ff, d, E, kStreamGrid, stream, fd);
 }
 
 hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,

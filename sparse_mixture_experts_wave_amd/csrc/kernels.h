@@ -59,6 +59,15 @@ hipError_t launch_stream_up_bf16(const uint16_t* x, const int32_t* offsets, cons
 hipError_t launch_stream_down_bf16(const uint16_t* h, const int32_t* offsets, const uint16_t* w2,
                                    const uint16_t* b2, float* y_sorted, int64_t T, int d, int d_ff,
                                    int E, hipStream_t stream);
+// The streaming up projection with the dispatch folded in, for decode-size
+// layers (stream_dispatch_supported: T * k <= 64 pairs, E <= 64): it sorts the
+// router's topk_idx [T][k] itself and stores offsets, sorted_token and inv_pos
+// as launch_dispatch would, so no dispatch launch precedes it.
+bool stream_dispatch_supported(int64_t T, int k, int d, int d_ff, int E);
+hipError_t launch_stream_up_dispatch_bf16(const uint16_t* x, const int32_t* topk_idx, int k, int32_t* offsets,
+                                          int32_t* sorted_token, int32_t* inv_pos, const uint16_t* w1,
+                                          const uint16_t* w3, const uint16_t* b1, const uint16_t* b3, uint16_t* h,
+                                          int64_t T, int d, int d_ff, int E, hipStream_t stream);
 
 // Prefill-regime grouped MFMA GEMMs (expert_gemm.hip).
 hipError_t launch_gemm_up_bf16(const uint16_t* x, const int32_t* offsets, const int32_t* sorted_token,

@@ -155,14 +155,27 @@ moe_status check_bias(const moe_expert_bias* eb) {
   return optional(eb->b2, "expert_bias->b2");
 }
 
+// Dispatch folded into the up projection: the router's choices in, the
+// permutation (offsets, sorted_token, inv_pos) written by that kernel.
+struct FusedDispatchArgs {
+  const int32_t* topk_idx;
+  int32_t* inv_pos;
+};
+
 moe_status run_ffn(const moe_shape* s, const void* x, const int32_t* off, const int32_t* st,
                    const void* w1, const void* w3, const void* w2, const moe_expert_bias* eb, float* y_sorted,
-                   void* h, float* part, void* stream, bool timed) {
+                   void* h, float* part, void* stream, bool timed, const FusedDispatchArgs* fused = nullptr) {
   const void* b1 = eb ? eb->b1 : nullptr;
   const void* b3 = eb ? eb->b3 : nullptr;
   const void* b2 = eb ? eb->b2 : nullptr;
   hipError_t err;
-  if (s->wt == MOE_BF16) {
+  if (fused != nullptr) {
+    err = moe::launch_stream_up_dispatch_bf16(static_cast<const uint16_t*>(x), fused->topk_idx, s->k,
+                                              const_cast<int32_t*>(off), const_cast<int32_t*>(st), fused->inv_pos,
+                                              static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w3),
+                                              static_cast<const uint16_t*>(b1), static_cast<const uint16_t*>(b3),
+                                              static_cast<uint16_t*>(h), s->T, s->d, s->d_ff, s->E, hs(stream));
+  } else if (s->wt == MOE_BF16) {
     err = moe::launch_expert_up_bf16(static_cast<const uint16_t*>(x), off, st, static_cast<const uint16_t*>(w1),
                                      static_cast<const uint16_t*>(w3), static_cast<const uint16_t*>(b1),
                                      static_cast<const uint16_t*>(b3), static_cast<uint16_t*>(h), s->T, s->k,
@@ -208,13 +221,18 @@ moe_status forward_impl(const moe_shape* s, const void* x, const float* w_gate, 
     u = at<void>(ws, L.u);
     xin = u;
   }
+  // Decode-size bf16 layers sort the router's choices inside the streaming up
+  // projection instead of in a dispatch launch of their own.
+  const bool fuse = s->wt == MOE_BF16 && moe::stream_dispatch_supported(s->T, s->k, s->d, s->d_ff, s->E);
+  const FusedDispatchArgs fused{idx, inv};
   MOE_TRY(mark(0, stream));
   MOE_TRY(run_route(s, x, w_gate, bias, nullptr, idx, w, gamma, eps, u, stream));
   MOE_TRY(mark(1, stream));
-  MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
+  if (!fuse)
+    MOE_TRY(hip_status(moe::launch_dispatch(idx, s->T, s->k, s->E, off, st, inv, hs(stream)), "dispatch launch"));
   MOE_TRY(mark(2, stream));
   float* part = (with_part && part_bytes(s)) ? at<float>(ws, L.part) : nullptr;
-  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, part, stream, true));
+  MOE_TRY(run_ffn(s, xin, off, st, w1, w3, w2, eb, ys, h, part, stream, true, fuse ? &fused : nullptr));
   MOE_TRY(mark(4, stream));
   MOE_TRY(hip_status(moe::launch_combine(ys, inv, w, residual, y, s->act == MOE_BF16, s->T, s->k, s->d, hs(stream)),
                      "combine launch"));
