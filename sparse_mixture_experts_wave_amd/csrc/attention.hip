@@ -289,13 +289,14 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                      vrs, __umul24(static_cast<uint32_t>(min(kv0 + 2 * kg + i, T - 1)), row_bytes) + vchunk, 0, 0));
   };
-  auto store_k = [&](int buf) {
+  auto store_k_from = [&](int buf, const u32x4 (&src)[FA_KC]) {
 #pragma unroll
     for (int i = 0; i < FA_KC; ++i) {
       const int c = tid * FA_KC + i;
-      store16(&Ks[buf][kpad(c >> 4, c & 15)], kr[i]);
+      store16(&Ks[buf][kpad(c >> 4, c & 15)], src[i]);
     }
   };
+  auto store_k = [&](int buf) { store_k_from(buf, kr); };
   auto store_v = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -411,15 +412,18 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     __syncthreads();
   };
 
-  // Prologue: K(0), V(0) and K(1) into LDS, then S^T of tile 0.
+  // Prologue: K(0), V(0) and K(1) into LDS, then S^T of tile 0.  The three
+  // loads go out together (K(1) into spare registers; rows clamped like every
+  // tile's), so the workgroup waits for one memory round trip, not two.
+  u32x4 k1[FA_KC];
+  load_k(FA_BKV);
+  k1[0] = kr[0];
+  k1[1] = kr[1];
   load_k(0);
   load_v(0);
   store_k(0);
   store_v(0);
-  if (ntiles > 1) {
-    load_k(FA_BKV);
-    store_k(1);
-  }
+  store_k_from(1, k1);
   __syncthreads();
   f32x16 sA[2], sB[2];
   s_half(sA, 0, 0);
@@ -429,14 +433,37 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     if (j + 1 < ntiles) tile(j + 1, sB, sA);
   }
 
-  // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4.
-  if (my_q < T) {
+  // O^T accumulator: lane holds query my_q, dims 32 db + 8 (e / 4) + 4 half + e % 4,
+  // so each group of four e is four adjacent dims.  The wave's 32 x 128 block
+  // of O goes through LDS (the K / V buffers are free after the last tile's
+  // barrier: waves 0-3 use Ks, 4-7 Vt, 32 rows of 272 bytes each) and out as
+  // whole 256-byte rows, four per store instruction.  Stored straight from the
+  // accumulator layout, every store instruction touched 32 rows and the
+  // workgroup's stores took several microseconds to drain.
+  {
     const float inv = 1.0f / l;
-    uint16_t* op = o + static_cast<int64_t>(my_q) * ld_q + h * FA_D;
+    static_assert(FA_NW / 2 * FA_QW * FA_LD * 2 <= static_cast<int>(sizeof(Ks)), "O staging exceeds Ks");
+    static_assert(FA_NW / 2 * FA_QW * FA_LD * 2 <= static_cast<int>(sizeof(Vt)), "O staging exceeds Vt");
+    uint16_t* stage = (wave < FA_NW / 2 ? &Ks[0][0] : &Vt[0][0]) + (wave % (FA_NW / 2)) * FA_QW * FA_LD;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) op[db * 32 + 8 * (e >> 2) + 4 * half + (e & 3)] = f32_to_bf16(oacc[db][e] * inv);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int e = 4 * g4;
+        uint2 w;
+        w.x = cvt_pk_bf16(oacc[db][e] * inv, oacc[db][e + 1] * inv);
+        w.y = cvt_pk_bf16(oacc[db][e + 2] * inv, oacc[db][e + 3] * inv);
+        *reinterpret_cast<uint2*>(&stage[(lane & 31) * FA_LD + db * 32 + 8 * g4 + 4 * half]) = w;
+      }
+    __syncthreads();
+    // Store instruction i: rows 4 i + lane / 16 of the wave, 16-byte chunk lane % 16.
+#pragma unroll
+    for (int i = 0; i < FA_QW / 4; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int c = lane & 15;
+      const u32x4 v = load16(&stage[r * FA_LD + 8 * c]);
+      if (qw + r < T) store16(o + static_cast<int64_t>(qw + r) * ld_q + h * FA_D + 8 * c, v);
+    }
   }
 }
 
