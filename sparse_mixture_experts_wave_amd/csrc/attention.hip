@@ -221,6 +221,7 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     uint16_t* __restrict__ o, int T, int H, int G, float scale_log2) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][FA_BKV * FA_LD];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][FA_D * VT_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[FA_NW][FA_QW * FA_LD];
 
   // Workgroups go to the 8 XCDs in turn by linear id, and gridDim.x = H: with
   // H a multiple of 8, XCD x gets heads x H/8 .. x H/8 + H/8 - 1, so the heads
@@ -242,12 +243,15 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   // B operand of S^T = K Q^T: lane holds query my_q (clamped to T - 1; its
   // output is not stored), dims 16 ks + 8 half .. +7.
+  // Q goes through LDS: each wave loads its 32 rows four whole 256-byte rows
+  // per instruction (row 4 i + lane / 16, chunk lane % 16), and reads the
+  // operand layout back after the prologue's barrier.  Loaded straight into
+  // the operand layout, every load instruction touched 32 rows.
   bf16x8 qf[8];
-  {
-    const uint16_t* qp = q + static_cast<int64_t>(min(my_q, T - 1)) * ld_q + h * FA_D + 8 * half;
+  u32x4 qraw[FA_QW / 4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(load16(qp + 16 * ks));
-  }
+  for (int i = 0; i < FA_QW / 4; ++i)
+    qraw[i] = load16(q + static_cast<int64_t>(min(qw + 4 * i + (lane >> 4), T - 1)) * ld_q + h * FA_D + 8 * (lane & 15));
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -421,10 +425,14 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   k1[1] = kr[1];
   load_k(0);
   load_v(0);
+#pragma unroll
+  for (int i = 0; i < FA_QW / 4; ++i) store16(&Qs[wave][(4 * i + (lane >> 4)) * FA_LD + 8 * (lane & 15)], qraw[i]);
   store_k(0);
   store_v(0);
   store_k_from(1, k1);
   __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(load16(&Qs[wave][(lane & 31) * FA_LD + 16 * ks + 8 * half]));
   f32x16 sA[2], sB[2];
   s_half(sA, 0, 0);
   s_half(sA, 0, 1);
