@@ -60,8 +60,11 @@ __device__ __forceinline__ u32x4 load16_buf_nt(__amdgpu_buffer_rsrc_t rs, uint32
 
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// SiLU(z) = z / (1 + e^{-z}).
-__device__ __forceinline__ float silu_fast(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z / (1 + e^{-z}).  The fast form multiplies by the hardware
+// reciprocal (v_rcp_f32, about 1 ulp) instead of dividing: an IEEE division
+// is about ten vector instructions, and the up projection's epilogue forms
+// one SiLU per output.  The result is rounded to bf16 afterwards.
+__device__ __forceinline__ float silu_fast(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float silu_exact(float z) { return z / (1.0f + expf(-z)); }
 
 // Which expert owns global M-tile `tile` when expert e contributes
