@@ -178,13 +178,6 @@ constexpr int VT_STRIDE = FA_BKV + 8;    // 72 bf16 = 144 bytes per transposed V
 __device__ __forceinline__ uint32_t lo16(uint32_t w) { return w & 0xFFFFu; }
 __device__ __forceinline__ uint32_t hi16(uint32_t w) { return w >> 16; }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // 2^x with the hardware instruction alone (v_exp_f32): results below 2^-126
 // flush to zero instead of being rebuilt as denormals, which a softmax weight

@@ -76,6 +76,8 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -550,29 +552,56 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x4 (&acc)[8][
       return;
     }
   }
+  // The plain outputs.  The epilogue runs on every wave at once, after the
+  // main loop, so its vector instruction count is time the matrix cores
+  // stand idle: without biases the adds are left out, and the gated outputs
+  // are rounded two at a time (v_cvt_pk_bf16_f32, round to nearest even like
+  // f32_to_bf16) and stored from the halves of the packed word.
+  const bool has_bias = bias0 != nullptr || (GATED && bias1 != nullptr);
+  auto plain = [&](auto with_bias) {
+    constexpr bool B = decltype(with_bias)::value;
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = wm * 128 + mi * 16 + lr + v;
-      if (mi < 2 * mlo || mi >= 2 * mhi || r >= t.rows) continue;
-      const int64_t row = static_cast<int64_t>(t.m0 + r) * N;
+    for (int mi = 0; mi < 8; ++mi) {
+      if (mi < 2 * mlo || mi >= 2 * mhi) continue;
+      const int r0 = wm * 128 + mi * 16 + lr;  // rows r0 .. r0 + 3
       if constexpr (GATED) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const int n = col(nb);
-          if (n < N)
-            static_cast<uint16_t*>(out)[row + n] =
-                f32_to_bf16(silu_fast(acc[mi][nb][v] + bb[nb]) * (acc[mi][nb + 2][v] + bb[nb + 2]));
+          float y[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float g = B ? acc[mi][nb][v] + bb[nb] : acc[mi][nb][v];
+            const float u = B ? acc[mi][nb + 2][v] + bb[nb + 2] : acc[mi][nb + 2][v];
+            y[v] = silu_fast(g) * u;
+          }
+          const uint32_t p01 = cvt_pk_bf16(y[0], y[1]), p23 = cvt_pk_bf16(y[2], y[3]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const uint32_t p = v < 2 ? p01 : p23;
+            if (r0 + v < t.rows && n < N)
+              static_cast<uint16_t*>(out)[static_cast<int64_t>(t.m0 + r0 + v) * N + n] =
+                  static_cast<uint16_t>((v & 1) ? p >> 16 : p);
+          }
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = col(nb);
-          if (n < N) static_cast<float*>(out)[row + n] = acc[mi][nb][v] + bb[nb];
+        for (int v = 0; v < 4; ++v) {
+          if (r0 + v >= t.rows) continue;
+          const int64_t row = static_cast<int64_t>(t.m0 + r0 + v) * N;
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            const int n = col(nb);
+            if (n < N) static_cast<float*>(out)[row + n] = B ? acc[mi][nb][v] + bb[nb] : acc[mi][nb][v];
+          }
         }
       }
     }
+  };
+  if (has_bias)
+    plain(std::true_type{});
+  else
+    plain(std::false_type{});
 }
 
 // A thread's 128 accumulators as 32 float4 chunks (chunk 4 mi + nb is block
