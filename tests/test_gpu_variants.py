@@ -167,3 +167,29 @@ def test_mixtral_prefill_t4096_every_element():
     say(f"prefill T=4096 every element: max rel err {err:.3e} on {int(clear.sum())} tokens")
     assert clear.mean() > 0.95
     assert err <= BF16_TOL
+
+
+def test_mixtral_skewed_t16384_every_element():
+    """The Zipf-skewed workload (T = 16384, router bias ln p_e) as the benchmark
+    runs it: expert loads from about 11.5k rows down to about 1k, so every
+    expert ends in a ragged row tile; every output element of every clear token
+    against the oracle's expert-major form on the host."""
+    cfg = CONFIGS["mixtral_skewed_t16384"]
+    say("skewed T=16384 every element: generating")
+    dv = generate_torch(cfg, torch.device("cuda:0"))
+    y = moe.moe_forward(dv["x"], dv["w_gate"], dv["bias"], dv["w1"], dv["w3"], dv["w2"])
+    torch.cuda.synchronize()
+    y = to_host(y)
+    xh, wgh, bh = to_host(dv["x"]), to_host(dv["w_gate"]), to_host(dv["bias"])
+    w1, w3, w2 = to_host(dv["w1"]), to_host(dv["w3"]), to_host(dv["w2"])
+    del dv
+    say("skewed T=16384 every element: oracle")
+    y_ref, (g, idx, w) = oracle.moe_forward_expert_loop(xh, wgh, bh, w1, w3, w2)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    clear, _ = clear_tokens(g)
+    err = max_rel_err(y, y_ref, clear)
+    say(f"skewed T=16384 every element: rows per expert {counts.tolist()}, max rel err {err:.3e} "
+        f"on {int(clear.sum())} tokens")
+    assert counts.max() > 8 * counts.min()  # the skew is there
+    assert clear.mean() > 0.95
+    assert err <= BF16_TOL
