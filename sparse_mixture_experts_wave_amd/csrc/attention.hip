@@ -53,11 +53,17 @@ __device__ __forceinline__ float2 rope_angle(int64_t pos, int i, int dh, double 
 
 // With cs set, workgroup t also writes the angles of position pos0 + t for
 // the 64 pairs of a 128-wide head: cs[t][i], for the projection's epilogue.
+// Workgroup 0 also writes row_range = [0, T] (one grid row per token), the
+// offsets that let the expert GEMM run the projections as one expert owning
+// every row.
 __global__ __launch_bounds__(RN_T) void rmsnorm_rows_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ gamma, float eps,
                                                             uint16_t* __restrict__ u, int d,
+                                                            int32_t* __restrict__ row_range,
                                                             float2* __restrict__ cs, double theta, int64_t pos0) {
   static_assert(RN_T >= 64, "one thread per angle");
+  if (blockIdx.x == 0 && threadIdx.x < 2)
+    row_range[threadIdx.x] = threadIdx.x == 0 ? 0 : static_cast<int32_t>(gridDim.x);
   if (cs && threadIdx.x < 64)
     cs[static_cast<int64_t>(blockIdx.x) * 64 + threadIdx.x] =
         rope_angle(pos0 + blockIdx.x, static_cast<int>(threadIdx.x), 128, theta);
@@ -137,13 +143,6 @@ __global__ __launch_bounds__(256) void residual_add_kernel(uint16_t* __restrict_
   o[2] = pack_bf16x2(lo_bf16(w[2]) + b.x, hi_bf16(w[2]) + b.y);
   o[3] = pack_bf16x2(lo_bf16(w[3]) + b.z, hi_bf16(w[3]) + b.w);
   store16(h + 8 * i, o);
-}
-
-__global__ void row_range_kernel(int32_t* __restrict__ offsets, int32_t rows) {
-  if (threadIdx.x == 0) {
-    offsets[0] = 0;
-    offsets[1] = rows;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -471,8 +470,8 @@ __global__ __launch_bounds__(FA_NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 }  // namespace
 
 hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
-                               hipStream_t stream, float* cs, double theta, int64_t pos0) {
-  rmsnorm_rows_kernel<<<static_cast<unsigned>(T), RN_T, 0, stream>>>(x, gamma, eps, u, d,
+                               int32_t* row_range, hipStream_t stream, float* cs, double theta, int64_t pos0) {
+  rmsnorm_rows_kernel<<<static_cast<unsigned>(T), RN_T, 0, stream>>>(x, gamma, eps, u, d, row_range,
                                                                      reinterpret_cast<float2*>(cs), theta, pos0);
   return hipGetLastError();
 }
@@ -488,11 +487,6 @@ hipError_t launch_rope_pack(const float* qkv, uint16_t* q, uint16_t* k, uint16_t
 hipError_t launch_residual_add(uint16_t* h, const float* y, int64_t n, hipStream_t stream) {
   const int64_t n8 = n / 8;
   residual_add_kernel<<<static_cast<unsigned>((n8 + 255) / 256), 256, 0, stream>>>(h, y, n8);
-  return hipGetLastError();
-}
-
-hipError_t launch_row_range(int32_t* offsets, int64_t rows, hipStream_t stream) {
-  row_range_kernel<<<1, 64, 0, stream>>>(offsets, static_cast<int32_t>(rows));
   return hipGetLastError();
 }
 

@@ -95,21 +95,21 @@ int aux_loss_max_k();
 hipError_t launch_aux_loss(const float* logits, int64_t layers, int64_t T, int E, int k, const uint8_t* mask,
                            float alpha, float* loss, float* stats, hipStream_t stream);
 
-// Attention sublayer (attention.hip): row RMSNorm (bf16 -> bf16; with cs set
-// it also writes the RoPE table cs [T][64] (cos, sin) of positions pos0 + t
-// for d_h = 128), RoPE + split of the fused Q|K|V projection (fp32 -> bf16
-// head-major), causal GQA flash attention (bf16, d_h = 128), residual add
-// (h += y, one rounding), and the [0, rows] offsets that let the expert GEMM
-// run one dense projection.
+// Attention sublayer (attention.hip): row RMSNorm (bf16 -> bf16; it also
+// writes row_range = [0, T], the offsets that let the expert GEMM run one
+// dense projection, and with cs set the RoPE table cs [T][64] (cos, sin) of
+// positions pos0 + t for d_h = 128), RoPE + split of the fused Q|K|V
+// projection (fp32 -> bf16 head-major), causal GQA flash attention (bf16,
+// d_h = 128) and the residual add (h += y, one rounding).
 hipError_t launch_rmsnorm_rows(const uint16_t* x, const float* gamma, float eps, uint16_t* u, int64_t T, int d,
-                               hipStream_t stream, float* cs = nullptr, double theta = 0.0, int64_t pos0 = 0);
+                               int32_t* row_range, hipStream_t stream, float* cs = nullptr, double theta = 0.0,
+                               int64_t pos0 = 0);
 hipError_t launch_rope_pack(const float* qkv, uint16_t* q, uint16_t* k, uint16_t* v, int64_t T, int H, int G,
                             int dh, double theta, int64_t pos0, hipStream_t stream);
 bool flash_attn_supported(int dh);
 hipError_t launch_flash_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int64_t T,
                              int H, int G, int dh, hipStream_t stream);
 hipError_t launch_residual_add(uint16_t* h, const float* y, int64_t n, hipStream_t stream);
-hipError_t launch_row_range(int32_t* offsets, int64_t rows, hipStream_t stream);
 
 // Token count at or below which the bf16 expert FFN streams weights
 // (decode regime) instead of running the tiled grouped GEMM.

@@ -548,20 +548,20 @@ moe_status moe_attention_block_forward(const moe_attn_shape* shape, void* h_inou
   float* oproj = at<float>(ws, L.oproj);
   uint16_t* h = static_cast<uint16_t*>(h_inout);
   const hipStream_t st = hs(stream);
-  // The projections run on the experts' GEMM as a single expert owning all T rows.
-  MOE_TRY(hip_status(moe::launch_row_range(off, T, st), "row range launch"));
+  // The projections run on the experts' GEMM as a single expert owning all T
+  // rows: the RMSNorm kernel writes those offsets, [0, T], into `off`.
   float* part = L.part < L.total ? at<float>(ws, L.part) : nullptr;
   if (!moe::stream_supported(T, nqkv, d)) {
     // GEMM path: RoPE and the split into q, k, v run in the projection's epilogue.
     float* cs = at<float>(ws, L.cs);
-    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st, cs, static_cast<double>(rope_theta),
+    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, off, st, cs, static_cast<double>(rope_theta),
                                                 pos0),
                        "rmsnorm launch"));
     MOE_TRY(hip_status(moe::launch_gemm_qkv_rope_bf16(xn, off, static_cast<const uint16_t*>(wqkv), cs, q, k, v, T,
                                                       nq, G * dh, d, part, st),
                        "qkv projection launch"));
   } else {
-    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, st), "rmsnorm launch"));
+    MOE_TRY(hip_status(moe::launch_rmsnorm_rows(h, gamma, eps, xn, T, d, off, st), "rmsnorm launch"));
     MOE_TRY(hip_status(moe::launch_expert_down_bf16(xn, off, static_cast<const uint16_t*>(wqkv), nullptr, qkv, T, 1,
                                                     nqkv, d, 1, part, st),
                        "qkv projection launch"));
