@@ -639,8 +639,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2;
-  const int wn = wave & 3;
 
   // Copy sources.  Group 0: the activation rows (gathered through
   // sorted_token for the up projection; for the down projection the tile's
