@@ -774,6 +774,11 @@ hipError_t launch(const uint16_t* A, const int32_t* gather, const int32_t* offse
   // with at least 4 rounds for certain (ceil(rows / BM) * NT tiles at least)
   // nothing is split and the fix-up is not launched.
   if (((rows + BM - 1) / BM) * NT >= 4 * static_cast<int64_t>(cus)) part = nullptr;
+  // One expert owning every row (the attention projections) has exactly
+  // ceil(rows / BM) * NT tiles: when they fill whole rounds nothing is split,
+  // and the fix-up launch is skipped.  (Not splitting is correct for any
+  // offsets; it only leaves a partial last round unsplit.)
+  if (E == 1 && ((rows + BM - 1) / BM) * NT % cus == 0) part = nullptr;
   const int64_t units = part ? tiles + cus : tiles;
   float4* p4 = reinterpret_cast<float4*>(part);
   gemm_bf16_kernel<GATED><<<static_cast<unsigned>(units), NTHR, 0, s>>>(A, gather, offsets, E, B0, B1, bias0,
