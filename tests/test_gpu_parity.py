@@ -236,6 +236,25 @@ def test_expert_ffn_split_last_round(d, d_ff, counts):
     assert torch.equal(ys, again)  # the pieces are summed in a fixed order
 
 
+def test_expert_ffn_tile_row_boundaries():
+    """Every partial-tile case of the grouped GEMM in one call: experts whose
+    last 256-row tile holds 1, 15 .. 17, 31 .. 33, 127 .. 129 rows (16-row
+    blocks skipped), 223 .. 225 rows (the switch to the branch-free main loop
+    above 224) and 255 .. 257 rows, the rows gathered in a random order; rows
+    routed by hand, every row against the oracle."""
+    counts = [1, 15, 16, 17, 31, 32, 33, 127, 128, 129, 223, 224, 225, 255, 256, 257]
+    E, T, d, d_ff = len(counts), sum(counts), 256, 512
+    say(f"expert_ffn tile-row boundaries E={E} T={T}")
+    inp = generate(small("rowbound", T, d, d_ff, E=E))
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    st = np.random.default_rng(11).permutation(T).astype(np.int32)
+    ref = oracle.expert_rows_ref(inp["x"], st, off, inp["w1"], inp["w3"], inp["w2"])
+    ys = moe.moe_expert_ffn(to_dev(inp["x"]), to_dev(off), to_dev(st), to_dev(inp["w1"]), to_dev(inp["w3"]),
+                            to_dev(inp["w2"]), k=1)
+    torch.cuda.synchronize()
+    assert max_rel_err(to_host(ys), ref) <= BF16_TOL
+
+
 # ---------------------------------------------------------------------------
 # the whole layer
 # ---------------------------------------------------------------------------
